@@ -1,0 +1,152 @@
+/*
+ * mlaverify.h - C ABI of the DDTree MLA tree-verify attention library (gfx950).
+ *
+ * The operation (page "Chunk 66.0", magik.net llmopt segment 66, summary
+ * paragraph; page "Chunk 66.1", summary paragraph):
+ *   DDTree speculative decoding verifies a draft tree of T nodes per request
+ *   with one attention pass of the target model.  The attention is MLA in its
+ *   absorbed (latent) form: the H heads of one tensor-parallel rank (8 per rank
+ *   under TP8) all score against the same 576-wide bf16 latent row per token
+ *   (512 latent + 64 rope columns) and read their value from its first 512
+ *   columns.  KV rows live in a shared pool with page_size=1: every token is one
+ *   row, addressed through a per-request token-index table, so on a churned
+ *   pool the reads are scattered.  Node i of a request attends to every prefix
+ *   token of its request, to its ancestors in the tree and to itself.
+ *
+ *   For request b, node i, head h (sigma = sm_scale):
+ *     Vis(b,i) = prefix slots of b  ++  slots of {i, parent(i), parent(parent(i)), ...}
+ *     s_j      = sigma * sum_{d<576} q[b,i,h,d] * KV[j,d]
+ *     lse      = ln sum_{j in Vis} exp(s_j)
+ *     out      = sum_{j in Vis} exp(s_j - lse) * KV[j, 0:512]
+ *
+ *   The computation is split over the prefix (split-KV partials merged by their
+ *   log-sum-exp, the "partial+reduce" design of the Chunk 66.0 summary) and is
+ *   capture-safe in the sense of the Chunk 66.1 summary: mlaverify_run makes no
+ *   host synchronisation, no host<->device copy and no allocation, and works in
+ *   a caller-provided workspace, so it can be recorded into a HIP graph.
+ *
+ * Conventions
+ *   - Every function returns MLAVERIFY_OK (0) on success or a negative status
+ *     (see mlaverify_status_string).  On any host-detected error nothing is
+ *     enqueued and outputs are left untouched.
+ *   - All tensor pointers are DEVICE pointers on the handle's device; sizes and
+ *     shapes are host integers.  The caller owns every tensor; the library keeps
+ *     no pointer beyond a call except the workspace.
+ *   - Calls on one handle must be ordered on one stream (they share the
+ *     workspace); use one handle per concurrent stream.
+ */
+#ifndef MLAVERIFY_H
+#define MLAVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLAVERIFY_API __attribute__((visibility("default")))
+
+#define MLAVERIFY_LATENT_DIM 576 /* columns of a KV row used for scores */
+#define MLAVERIFY_V_DIM 512      /* leading columns of a KV row used as V */
+#define MLAVERIFY_MAX_TREE_NODES 64
+
+/* Status codes. */
+#define MLAVERIFY_OK 0
+#define MLAVERIFY_ERR_INVALID_ARG (-1)    /* null pointer, misalignment, size out of range */
+#define MLAVERIFY_ERR_UNSUPPORTED (-2)    /* a configuration the kernels do not implement */
+#define MLAVERIFY_ERR_NO_MEMORY (-3)      /* library-owned workspace allocation failed */
+#define MLAVERIFY_ERR_WORKSPACE (-4)      /* caller workspace smaller than mlaverify_workspace_bytes */
+#define MLAVERIFY_ERR_HIP (-5)            /* a HIP runtime call or kernel launch failed */
+
+/* Sticky device-side data-error bits (mlaverify_read_device_errors). */
+#define MLAVERIFY_DEVERR_BAD_PARENT 0x1u  /* a tree_parent entry outside [-1, node) */
+#define MLAVERIFY_DEVERR_BAD_INDEX 0x2u   /* a kv_indices entry outside [0, pool_slots) */
+#define MLAVERIFY_DEVERR_BAD_PREFIX 0x4u  /* a prefix_lens entry outside [0, max_prefix_len] */
+
+/* Flags for mlaverify_config.flags. */
+#define MLAVERIFY_FLAG_NO_FASTPATH 0x1u   /* always gather row by row (A/B tests of the contiguous path) */
+
+typedef struct mlaverify_handle* mlaverify_t;
+
+typedef struct mlaverify_config {
+  int32_t num_heads;       /* H: heads of this rank, 1..128 */
+  int32_t max_batch;       /* largest batch passed to run; sizes the grid and workspace */
+  int32_t max_tree_nodes;  /* largest T passed to run, 1..64 (one 64-bit ancestor mask per node) */
+  int32_t max_prefix_len;  /* largest P_b accepted; larger ones are device errors */
+  int64_t pool_slots;      /* rows in kv_pool; indices outside [0, pool_slots) are device errors */
+  int64_t kv_row_stride;   /* elements between consecutive pool rows, >= 576, multiple of 8 */
+  float sm_scale;          /* softmax scale sigma (e.g. 1/sqrt(192)) */
+  int32_t split_tokens;    /* 0: choose the prefix split length per call on the device;
+                              else a fixed split length in tokens, a multiple of 32 */
+  uint32_t flags;          /* MLAVERIFY_FLAG_* */
+} mlaverify_config;
+
+/* Checks a configuration without touching the GPU.  Returns MLAVERIFY_OK,
+ * MLAVERIFY_ERR_INVALID_ARG or MLAVERIFY_ERR_UNSUPPORTED. */
+MLAVERIFY_API int mlaverify_validate_config(const mlaverify_config* cfg);
+
+/* Bytes of device workspace a handle with this configuration needs (0 if the
+ * configuration is invalid).  Pure host computation. */
+MLAVERIFY_API size_t mlaverify_workspace_bytes(const mlaverify_config* cfg);
+
+/* Creates a handle on the current HIP device.  workspace: a device buffer of at
+ * least mlaverify_workspace_bytes(cfg) bytes, 256-byte aligned, owned by the
+ * caller and kept alive until mlaverify_destroy; or NULL, in which case the
+ * library allocates (and later frees) it.  The workspace needs no
+ * initialisation; create clears the small error area with a synchronous memset.
+ * On success *out receives the handle. */
+MLAVERIFY_API int mlaverify_create(const mlaverify_config* cfg, void* workspace,
+                                   size_t workspace_bytes, mlaverify_t* out);
+
+/* Enqueues one verify-attention pass on `stream` (a hipStream_t; NULL = default
+ * stream).  Host arguments: batch in [1, max_batch], tree_nodes in
+ * [1, max_tree_nodes].  Device arguments:
+ *   q           bf16 [batch*T, H, 576], row (b*T + i)*H + h, contiguous, 16-byte aligned
+ *   kv_pool     bf16 [pool_slots, kv_row_stride], 16-byte aligned; columns 0..575 are read
+ *   kv_indices  int32 [sum_b (P_b + T)]: request b's P_b prefix slots in order, then the T
+ *               slots holding the latents of tree nodes 0..T-1; requests back to back
+ *   prefix_lens int32 [batch]: P_b, 0 <= P_b <= max_prefix_len
+ *   tree_parent int32 [batch, T]: -1 for a root, else a node index smaller than the node
+ *   out         bf16 [batch*T, H, 512] (written), 16-byte aligned
+ *   lse         fp32 [batch*T, H] (written): natural-log sum of exp(scores)
+ * Data errors found on the device (see MLAVERIFY_DEVERR_*) never cause an
+ * out-of-bounds access: they set sticky bits and every output row of the
+ * offending request becomes NaN; other requests are unaffected.
+ * Never synchronises, copies to/from the host or allocates: graph-capturable. */
+MLAVERIFY_API int mlaverify_run(mlaverify_t h, int32_t batch, int32_t tree_nodes,
+                                const void* q, const void* kv_pool, const int32_t* kv_indices,
+                                const int32_t* prefix_lens, const int32_t* tree_parent,
+                                void* out, float* lse, void* stream);
+
+/* Builds the tree-ancestor bitmasks alone (the mask step of run, on its own):
+ * masks[b*T + i] bit j is set iff tree node j is node i or one of its ancestors.
+ * tree_parent int32 [batch, T] and masks uint64 [batch, T] are device pointers;
+ * err (device, uint32 [batch]) receives MLAVERIFY_DEVERR_BAD_PARENT per bad
+ * request, whose masks are then 0.  1 <= T <= 64.  Enqueued on `stream`. */
+MLAVERIFY_API int mlaverify_tree_masks(const int32_t* tree_parent, int32_t batch, int32_t tree_nodes,
+                                       uint64_t* masks, uint32_t* err, void* stream);
+
+/* Copies the work partition of the most recent run into host memory (synchronises
+ * `stream`; for tests and reports, not for graphs).  Writes up to `capacity`
+ * int32 values: [split_len, total_units, n_mtiles, then per request b:
+ * key_offset_b, prefix_len_b, first_unit_b, units_b, error_bits_b].
+ * Returns the number of values available (which may exceed capacity) or a
+ * negative status. */
+MLAVERIFY_API int mlaverify_read_plan(mlaverify_t h, int32_t batch, void* stream, int32_t* host_out,
+                                      int32_t capacity);
+
+/* Reads and clears the sticky device-error bits (synchronises `stream`). */
+MLAVERIFY_API int mlaverify_read_device_errors(mlaverify_t h, void* stream, uint32_t* flags);
+
+/* Releases the handle (and the workspace if the library allocated it). */
+MLAVERIFY_API int mlaverify_destroy(mlaverify_t h);
+
+/* Static text for a status code. */
+MLAVERIFY_API const char* mlaverify_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLAVERIFY_H */

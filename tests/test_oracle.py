@@ -1,0 +1,373 @@
+"""Pins of the CPU fp64 oracle against facts that do not come from the oracle itself.
+
+Each test names what fixes the expected value: a hand-derived fixture, a closed
+form, an identity of the mathematics, brute force, or a library routine that the
+special case reduces to (torch's scaled_dot_product_attention in float64 on the
+CPU).  None of these reuse the oracle's own ancestor walk or softmax code.
+"""
+
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import mla_tree_oracle as orc
+from workloads import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "tiny_tree.txt")
+SCALE = 1.0 / math.sqrt(192.0)
+
+
+def read_golden():
+    vals = {}
+    with open(GOLDEN) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, *rest = line.split()
+            vals[key] = [int(x, 0) for x in rest]
+    return vals
+
+
+def closure_masks(parents):
+    """Ancestor-or-self sets by transitive closure of the child->parent relation.
+
+    reach starts as I + A (A[i, p] = 1 when p is i's parent) and is squared until it
+    stops changing; a different algorithm from walking parent pointers.
+    """
+    t = len(parents)
+    reach = np.eye(t, dtype=np.int64)
+    for i, p in enumerate(parents):
+        if p >= 0:
+            reach[i, p] = 1
+    while True:
+        nxt = np.minimum(reach @ reach, 1)
+        if np.array_equal(nxt, reach):
+            break
+        reach = nxt
+    return reach.astype(bool)  # reach[i, j]: j is i or an ancestor of i
+
+
+def widen_f32(bits):
+    return synth.bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def sdpa_reference(cfg, visible):
+    """Per-request SDPA in float64 with an explicit boolean mask over [prefix ++ tree] keys.
+
+    ``visible(b)`` returns the [T, T] tree visibility matrix of request b.
+    """
+    t, h = cfg["tree_nodes"], cfg["heads"]
+    outs = []
+    off = 0
+    for b in range(cfg["batch"]):
+        p = int(cfg["prefix_lens"][b])
+        seg = cfg["kv_indices"][off:off + p + t]
+        off += p + t
+        keys = torch.from_numpy(widen_f32(cfg["pool"][seg, :576]))  # [P+T, 576]
+        qb = torch.from_numpy(widen_f32(cfg["q"][b * t:(b + 1) * t]))  # [T, H, 576]
+        mask = torch.zeros(t, p + t, dtype=torch.bool)
+        mask[:, :p] = True
+        mask[:, p:] = torch.from_numpy(visible(b))
+        qh = qb.permute(1, 0, 2).unsqueeze(0)  # [1, H, T, 576]
+        k = keys.unsqueeze(0).unsqueeze(0).expand(1, h, p + t, 576)
+        v = keys[:, :512].unsqueeze(0).unsqueeze(0).expand(1, h, p + t, 512)
+        o = torch.nn.functional.scaled_dot_product_attention(
+            qh, k, v, attn_mask=mask.unsqueeze(0).unsqueeze(0), scale=SCALE)
+        outs.append(o[0].permute(1, 0, 2).numpy())  # [T, H, 512]
+    return np.concatenate(outs, axis=0)
+
+
+# --------------------------------------------------------------------------- masks
+
+def test_tiny_masks_match_hand_derivation():
+    g = read_golden()
+    masks = orc.ancestor_masks(np.array(g["parents"]))
+    assert [int(m) for m in masks] == g["masks"]
+    slots = [len(orc.visible_slots(np.arange(264), np.array([256]), np.array([g["parents"]]), 0, i))
+             for i in range(8)]
+    assert slots == g["visible"]
+    assert list(synth.tree_depths(g["parents"])) == g["depth"]
+
+
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("kind", ["random", "chain", "forest"])
+def test_masks_match_transitive_closure(seed, kind):
+    rng = np.random.default_rng(seed)
+    t = int(rng.integers(1, 65))
+    if kind == "random":
+        parents = synth.random_tree(rng, t)
+    elif kind == "chain":
+        parents = synth.chain_tree(t)
+    else:
+        parents = np.array([int(rng.integers(-1, i)) for i in range(t)], dtype=np.int32)
+    masks = orc.ancestor_masks(parents)
+    reach = closure_masks(parents)
+    for i in range(t):
+        bits = [(int(masks[i]) >> j) & 1 for j in range(t)]
+        assert bits == reach[i].astype(int).tolist()
+        assert int(masks[i]) >> t == 0
+
+
+def test_invalid_parent_rejected():
+    with pytest.raises(ValueError):
+        orc.ancestor_masks(np.array([-1, 0, 2]))  # node 2 is its own parent
+    with pytest.raises(ValueError):
+        orc.ancestor_masks(np.array([0]))  # root must be -1
+    with pytest.raises(ValueError):
+        orc.ancestor_masks(np.array([-1, -2]))
+
+
+def test_random_tree_depth_bound():
+    rng = np.random.default_rng(7)
+    for _ in range(50):
+        parents = synth.random_tree(rng, 64)
+        assert parents[0] == -1
+        assert all(-1 <= p < i for i, p in enumerate(parents))
+        assert synth.tree_depths(parents).max() <= 8
+
+
+# --------------------------------------------------------------------------- inputs
+
+def test_bf16_widening_known_values():
+    bits = np.array([0x3F80, 0xC000, 0x0001, 0x7F80, 0xFF80, 0x3E4D, 0x0000, 0x8000], dtype=np.uint16)
+    v = orc.bf16_to_f64(bits)
+    assert v[0] == 1.0 and v[1] == -2.0
+    assert v[2] == 2.0 ** -133  # smallest bf16 subnormal
+    assert v[3] == math.inf and v[4] == -math.inf
+    assert v[5] == 0.2001953125  # 0x3E4D = 1.6015625 * 2^-3
+    assert v[6] == 0.0 and math.copysign(1.0, v[7]) == -1.0
+    assert np.isnan(orc.bf16_to_f64(np.array([0x7FC0], dtype=np.uint16)))[0]
+
+
+def test_f32_to_bf16_round_to_nearest_even():
+    x = np.array([1.0, 1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, 1.0 + 2.0 ** -8 + 2.0 ** -20, -2.5,
+                  3.0e38, np.inf, np.nan], dtype=np.float32)
+    b = synth.f32_to_bf16_bits(x)
+    assert b[0] == 0x3F80
+    assert b[1] == 0x3F80  # tie -> even
+    assert b[2] == 0x3F82  # tie -> even (up)
+    assert b[3] == 0x3F81  # above the tie -> up
+    assert b[4] == 0xC020
+    assert b[5] == 0x7F62  # 3e38 rounds within range
+    assert b[6] == 0x7F80
+    assert (b[7] & 0x7F80) == 0x7F80 and (b[7] & 0x007F) != 0
+
+
+def test_generator_is_deterministic_and_shaped():
+    a = synth.make_config(0)
+    b = synth.make_config(0)
+    for k in ("q", "pool", "kv_indices", "prefix_lens", "tree_parent"):
+        assert np.array_equal(a[k], b[k])
+    assert a["q"].shape == (8, 8, 576) and a["pool"].shape == (512, 576)
+    assert np.array_equal(a["kv_indices"], np.arange(264))
+    assert a["tree_parent"].tolist() == [[-1, 0, 1, 2, 0, 4, 1, 6]]
+    c = synth.make_config(1)
+    assert len(np.unique(c["kv_indices"])) == len(c["kv_indices"]) == 4096 + 64
+    assert c["kv_indices"].max() < 262144
+    std = synth.bf16_bits_to_f32(c["q"]).std()
+    assert 0.09 < std < 0.11
+
+
+def test_batch_prefix_lengths_log_uniform_range():
+    rng_cfg = synth.CONFIGS[4]
+    lo, hi = rng_cfg["prefix"][1], rng_cfg["prefix"][2]
+    lens = synth._draw_prefix_lens(np.random.default_rng(0), rng_cfg["prefix"], 4000)
+    assert lens.min() >= lo and lens.max() <= hi
+    # log-uniform: the median of log-length sits at the midpoint of [ln lo, ln hi]
+    mid = 0.5 * (math.log(lo) + math.log(hi))
+    assert abs(np.median(np.log(lens)) - mid) < 0.15
+
+
+# --------------------------------------------------------------------------- closed forms
+
+def test_q_zero_closed_form_tiny():
+    """q = 0: every score is 0, so lse = ln(#visible) and out = plain mean of the visible V rows."""
+    g = read_golden()
+    cfg = synth.make_config(0, variant="qzero")
+    out, lse = orc.verify_attention(cfg["q"], cfg["pool"], cfg["kv_indices"], cfg["prefix_lens"],
+                                    cfg["tree_parent"], SCALE)
+    v = widen_f32(cfg["pool"][:, :512])
+    for i in range(8):
+        rows = list(range(256)) + [256 + j for j in range(8) if (g["masks"][i] >> j) & 1]
+        assert len(rows) == g["visible"][i]
+        np.testing.assert_allclose(lse[i], math.log(g["visible"][i]), rtol=0, atol=1e-13)
+        np.testing.assert_allclose(out[i], np.broadcast_to(v[rows].mean(axis=0), (8, 512)),
+                                   rtol=0, atol=1e-14)
+    # printed values in the fixture
+    assert abs(lse[0, 0] - 5.5490760848952201) < 1e-13
+    assert abs(lse[3, 0] - 5.5606816310155276) < 1e-13
+
+
+def test_constant_keys_closed_form():
+    """Every pool row equal to k: out = k[:512] and lse = sigma*q.k + ln(#visible)."""
+    cfg = synth.small_config(3, batch=2, prefix=[5, 0], tree_nodes=6, heads=3, slots=64)
+    k = cfg["pool"][7].copy()
+    cfg["pool"] = np.broadcast_to(k, cfg["pool"].shape).copy()
+    out, lse = orc.verify_attention(cfg["q"], cfg["pool"], cfg["kv_indices"], cfg["prefix_lens"],
+                                    cfg["tree_parent"], SCALE)
+    kf = [float(x) for x in widen_f32(k)]
+    for b in range(2):
+        reach = closure_masks(cfg["tree_parent"][b])
+        for i in range(6):
+            count = int(cfg["prefix_lens"][b]) + int(reach[i].sum())
+            for hh in range(3):
+                qv = [float(x) for x in widen_f32(cfg["q"][b * 6 + i, hh])]
+                dot = math.fsum(a * c for a, c in zip(qv, kf))
+                assert abs(lse[b * 6 + i, hh] - (SCALE * dot + math.log(count))) < 1e-12
+                np.testing.assert_allclose(out[b * 6 + i, hh], kf[:512], rtol=1e-13, atol=1e-15)
+
+
+# --------------------------------------------------------------------------- brute force / library
+
+@pytest.mark.parametrize("seed,prefix,tree", [
+    (0, [17, 3], "random"), (1, [0, 9], "forest"), (2, [11], "chain"), (3, [4, 0, 6], "random"),
+])
+def test_matches_brute_force(seed, prefix, tree):
+    cfg = synth.small_config(seed, batch=len(prefix), prefix=prefix, tree_nodes=5, heads=2,
+                             slots=96, tree=tree, q_scale=2.0)
+    out, lse = orc.verify_attention(cfg["q"], cfg["pool"], cfg["kv_indices"], cfg["prefix_lens"],
+                                    cfg["tree_parent"], SCALE)
+    bout, blse = orc.brute_force_verify_attention(cfg["q"], cfg["pool"], cfg["kv_indices"],
+                                                  cfg["prefix_lens"], cfg["tree_parent"], SCALE)
+    np.testing.assert_allclose(lse, blse, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(out, bout, rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("seed,tree,t", [(0, "random", 8), (1, "random", 64), (2, "forest", 13),
+                                         (3, "chain", 9)])
+def test_matches_torch_sdpa_float64(seed, tree, t):
+    cfg = synth.small_config(seed, batch=2, prefix=[40, 3], tree_nodes=t, heads=4, slots=4096,
+                             tree=tree, q_scale=1.0)
+    out, _ = orc.verify_attention(cfg["q"], cfg["pool"], cfg["kv_indices"], cfg["prefix_lens"],
+                                  cfg["tree_parent"], SCALE)
+    ref = sdpa_reference(cfg, lambda b: closure_masks(cfg["tree_parent"][b]))
+    np.testing.assert_allclose(out, ref, rtol=1e-11, atol=1e-13)
+
+
+def test_tiny_workload_matches_sdpa():
+    cfg = synth.make_config(0)
+    out, _ = orc.verify_attention(cfg["q"], cfg["pool"], cfg["kv_indices"], cfg["prefix_lens"],
+                                  cfg["tree_parent"], SCALE)
+    g = read_golden()
+    vis = np.array([[(m >> j) & 1 for j in range(8)] for m in g["masks"]], dtype=bool)
+    ref = sdpa_reference(cfg, lambda b: vis)
+    np.testing.assert_allclose(out, ref, rtol=1e-11, atol=1e-13)
+
+
+def test_chain_tree_equals_causal_attention():
+    """A chain tree is causal attention over prefix ++ tree, read off the last T rows."""
+    cfg = synth.small_config(5, batch=1, prefix=[30], tree_nodes=12, heads=2, slots=1024,
+                             tree="chain", q_scale=1.0)
+    out, _ = orc.verify_attention(cfg["q"], cfg["pool"], cfg["kv_indices"], cfg["prefix_lens"],
+                                  cfg["tree_parent"], SCALE)
+    p, t = 30, 12
+    keys = torch.from_numpy(widen_f32(cfg["pool"][cfg["kv_indices"], :576]))
+    qfull = torch.zeros(2, p + t, 576, dtype=torch.float64)
+    qfull[:, p:] = torch.from_numpy(widen_f32(cfg["q"])).permute(1, 0, 2)
+    o = torch.nn.functional.scaled_dot_product_attention(
+        qfull.unsqueeze(0), keys.expand(1, 2, p + t, 576), keys[:, :512].expand(1, 2, p + t, 512),
+        is_causal=True, scale=SCALE)
+    ref = o[0, :, p:].permute(1, 0, 2).numpy()
+    np.testing.assert_allclose(out, ref, rtol=1e-11, atol=1e-13)
+
+
+def test_single_node_is_plain_decode():
+    """T = 1: the node sees the whole prefix and itself, i.e. unmasked attention over P+1 keys."""
+    cfg = synth.small_config(6, batch=3, prefix=[50, 0, 7], tree_nodes=1, heads=5, slots=512,
+                             q_scale=1.0)
+    out, lse = orc.verify_attention(cfg["q"], cfg["pool"], cfg["kv_indices"], cfg["prefix_lens"],
+                                    cfg["tree_parent"], SCALE)
+    off = 0
+    for b, p in enumerate(cfg["prefix_lens"]):
+        keys = torch.from_numpy(widen_f32(cfg["pool"][cfg["kv_indices"][off:off + p + 1], :576]))
+        off += p + 1
+        qb = torch.from_numpy(widen_f32(cfg["q"][b])).unsqueeze(1)  # [H, 1, 576]
+        o = torch.nn.functional.scaled_dot_product_attention(
+            qb, keys.expand(5, p + 1, 576), keys[:, :512].expand(5, p + 1, 512), scale=SCALE)
+        np.testing.assert_allclose(out[b], o[:, 0].numpy(), rtol=1e-11, atol=1e-13)
+    assert np.all(np.isfinite(lse))
+
+
+# --------------------------------------------------------------------------- identities
+
+def test_permuted_pool_gives_identical_result():
+    cfg = synth.small_config(8, batch=2, prefix=[33, 21], tree_nodes=9, heads=3, slots=256)
+    perm = synth.permute_pool(cfg, np.random.default_rng(99))
+    a = orc.verify_attention(cfg["q"], cfg["pool"], cfg["kv_indices"], cfg["prefix_lens"],
+                             cfg["tree_parent"], SCALE)
+    b = orc.verify_attention(perm["q"], perm["pool"], perm["kv_indices"], perm["prefix_lens"],
+                             perm["tree_parent"], SCALE)
+    assert not np.array_equal(cfg["kv_indices"], perm["kv_indices"])
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_any_split_merged_by_lse_equals_single_pass():
+    cfg = synth.small_config(9, batch=2, prefix=[70, 12], tree_nodes=7, heads=2, slots=512,
+                             q_scale=1.5)
+    out, lse = orc.verify_attention(cfg["q"], cfg["pool"], cfg["kv_indices"], cfg["prefix_lens"],
+                                    cfg["tree_parent"], SCALE)
+    rng = np.random.default_rng(3)
+    for b in range(2):
+        for i in range(7):
+            slots = orc.visible_slots(cfg["kv_indices"], cfg["prefix_lens"], cfg["tree_parent"], b, i)
+            qrows = widen_f32(cfg["q"][b * 7 + i])
+            cuts = np.sort(rng.integers(0, len(slots) + 1, size=4))
+            parts = np.split(slots, cuts)  # may include empty parts
+            outs, lses = zip(*[orc.attention_over_slots(qrows, cfg["pool"], s, SCALE) for s in parts])
+            mo, ml = orc.lse_merge(outs, lses)
+            np.testing.assert_allclose(ml, lse[b * 7 + i], rtol=0, atol=1e-12)
+            np.testing.assert_allclose(mo, out[b * 7 + i], rtol=1e-12, atol=1e-14)
+
+
+def test_merge_of_nothing_is_empty():
+    o, l = orc.lse_merge([np.zeros((2, 512))] * 3, [np.full(2, -np.inf)] * 3)
+    assert np.all(np.isneginf(l)) and np.all(o == 0)
+
+
+def test_softmax_rows_sum_to_one():
+    cfg = synth.small_config(10, batch=1, prefix=[100], tree_nodes=16, heads=4, slots=512, q_scale=3.0)
+    for i in (0, 5, 15):
+        w = orc.attention_weights(cfg["q"], cfg["pool"], cfg["kv_indices"], cfg["prefix_lens"],
+                                  cfg["tree_parent"], SCALE, 0, i)
+        np.testing.assert_allclose(w.sum(axis=1), 1.0, rtol=0, atol=1e-12)
+        assert np.all(w >= 0)
+
+
+def test_prefix_order_invariance():
+    cfg = synth.small_config(11, batch=2, prefix=[64, 31], tree_nodes=8, heads=2, slots=512)
+    shuf = synth.permute_prefix(cfg, np.random.default_rng(5))
+    a = orc.verify_attention(cfg["q"], cfg["pool"], cfg["kv_indices"], cfg["prefix_lens"],
+                             cfg["tree_parent"], SCALE)
+    b = orc.verify_attention(shuf["q"], shuf["pool"], shuf["kv_indices"], shuf["prefix_lens"],
+                             shuf["tree_parent"], SCALE)
+    np.testing.assert_allclose(a[0], b[0], rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(a[1], b[1], rtol=0, atol=1e-12)
+
+
+def test_needle_dominates_where_visible():
+    cfg = synth.small_config(12, batch=2, prefix=[40, 25], tree_nodes=10, heads=2, slots=512)
+    cfg = synth.apply_variant(cfg, "needle_tree", np.random.default_rng(4))
+    out, lse = orc.verify_attention(cfg["q"], cfg["pool"], cfg["kv_indices"], cfg["prefix_lens"],
+                                    cfg["tree_parent"], SCALE)
+    for b in range(2):
+        needle = widen_f32(cfg["pool"][cfg["needle_slots"][b], :512])
+        reach = closure_masks(cfg["tree_parent"][b])
+        for i in range(10):
+            if reach[i, 1]:
+                np.testing.assert_allclose(out[b * 10 + i], np.broadcast_to(needle, (2, 512)), atol=1e-6)
+            else:
+                assert np.abs(out[b * 10 + i]).max() < 0.5
+
+
+def test_sharp_queries_still_match_brute_force():
+    cfg = synth.small_config(13, batch=1, prefix=[20], tree_nodes=4, heads=2, slots=64, q_scale=3.0)
+    out, lse = orc.verify_attention(cfg["q"], cfg["pool"], cfg["kv_indices"], cfg["prefix_lens"],
+                                    cfg["tree_parent"], SCALE)
+    bout, blse = orc.brute_force_verify_attention(cfg["q"], cfg["pool"], cfg["kv_indices"],
+                                                  cfg["prefix_lens"], cfg["tree_parent"], SCALE)
+    np.testing.assert_allclose(lse, blse, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(out, bout, rtol=1e-12, atol=1e-14)
