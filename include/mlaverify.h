@@ -62,7 +62,9 @@ extern "C" {
 /* Sticky device-side data-error bits (mlaverify_read_device_errors). */
 #define MLAVERIFY_DEVERR_BAD_PARENT 0x1u  /* a tree_parent entry outside [-1, node) */
 #define MLAVERIFY_DEVERR_BAD_INDEX 0x2u   /* a kv_indices entry outside [0, pool_slots) */
-#define MLAVERIFY_DEVERR_BAD_PREFIX 0x4u  /* a prefix_lens entry outside [0, max_prefix_len] */
+#define MLAVERIFY_DEVERR_BAD_PREFIX 0x4u  /* a prefix_lens entry outside [0, max_prefix_len]; that
+                                             request and every later one of the batch are poisoned,
+                                             since their index segments can no longer be located */
 
 /* Flags for mlaverify_config.flags. */
 #define MLAVERIFY_FLAG_NO_FASTPATH 0x1u   /* always gather row by row (A/B tests of the contiguous path) */
@@ -111,8 +113,9 @@ MLAVERIFY_API int mlaverify_create(const mlaverify_config* cfg, void* workspace,
  *   out         bf16 [batch*T, H, 512] (written), 16-byte aligned
  *   lse         fp32 [batch*T, H] (written): natural-log sum of exp(scores)
  * Data errors found on the device (see MLAVERIFY_DEVERR_*) never cause an
- * out-of-bounds access: they set sticky bits and every output row of the
- * offending request becomes NaN; other requests are unaffected.
+ * out-of-bounds access: they set sticky bits and every output row (out and lse)
+ * of the offending request becomes NaN; other requests are unaffected, except
+ * that a bad prefix length also poisons the requests after it.
  * Never synchronises, copies to/from the host or allocates: graph-capturable. */
 MLAVERIFY_API int mlaverify_run(mlaverify_t h, int32_t batch, int32_t tree_nodes,
                                 const void* q, const void* kv_pool, const int32_t* kv_indices,
@@ -138,6 +141,16 @@ MLAVERIFY_API int mlaverify_read_plan(mlaverify_t h, int32_t batch, void* stream
 
 /* Reads and clears the sticky device-error bits (synchronises `stream`). */
 MLAVERIFY_API int mlaverify_read_device_errors(mlaverify_t h, void* stream, uint32_t* flags);
+
+/* Kernel timing for benchmarks (not for graph capture).  After
+ * mlaverify_profile_begin(h, n) the next n calls of mlaverify_run record HIP events
+ * on their stream before and after each of their three kernels (plan, partial,
+ * merge).  mlaverify_profile_end synchronises on the last event, writes
+ * host_ms[3*i + k] = duration in milliseconds of kernel k of recorded run i for
+ * i < min(runs, capacity_runs), releases the events and returns the number of runs
+ * recorded (or a negative status).  begin while a session is open restarts it. */
+MLAVERIFY_API int mlaverify_profile_begin(mlaverify_t h, int32_t max_runs);
+MLAVERIFY_API int mlaverify_profile_end(mlaverify_t h, float* host_ms, int32_t capacity_runs);
 
 /* Releases the handle (and the workspace if the library allocated it). */
 MLAVERIFY_API int mlaverify_destroy(mlaverify_t h);

@@ -1,0 +1,329 @@
+// Host side of the C ABI declared in include/mlaverify.h: configuration checks,
+// workspace layout, grid sizing and the launch sequence of one verify pass.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <new>
+#include <vector>
+
+#include "mlaverify.h"
+#include "mlv_internal.h"
+
+using namespace mlv;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int mtiles_for(int heads, int T) { return (int)cdiv((int64_t)heads * T, kRowsPerBlock); }
+
+int target_units_for(int n_mtiles) { return (int)(cdiv(kTargetBlocks, n_mtiles) > 0 ? cdiv(kTargetBlocks, n_mtiles) : 1); }
+
+// Largest number of split units a run with `batch` requests of `T` nodes can produce.
+int units_for(const mlaverify_config& c, int batch, int T) {
+  if (c.split_tokens > 0) return batch * (int)(c.max_prefix_len > 0 ? cdiv(c.max_prefix_len, c.split_tokens) : 1);
+  return target_units_for(mtiles_for(c.num_heads, T)) + batch;
+}
+
+struct Layout {
+  size_t hdr, req, unit_tab, masks, part_lse, part_o, total;
+  int units_cap;      // entries of unit_tab
+  int64_t rows_cap;   // rows of part_o / part_lse
+};
+
+Layout layout_for(const mlaverify_config& c) {
+  Layout L;
+  int units_cap = 0;
+  int64_t rows_cap = 0;
+  for (int T = 1; T <= c.max_tree_nodes; T++) {
+    const int u = units_for(c, c.max_batch, T);
+    if (u > units_cap) units_cap = u;
+    const int64_t rows = (int64_t)u * c.num_heads * T;
+    if (rows > rows_cap) rows_cap = rows;
+  }
+  L.units_cap = units_cap;
+  L.rows_cap = rows_cap;
+  size_t off = 0;
+  L.hdr = off;       off = align_up(off + sizeof(PlanHeader));
+  L.req = off;       off = align_up(off + sizeof(ReqPlan) * (size_t)c.max_batch);
+  L.unit_tab = off;  off = align_up(off + sizeof(int32_t) * (size_t)units_cap);
+  L.masks = off;     off = align_up(off + sizeof(uint64_t) * (size_t)c.max_batch * c.max_tree_nodes);
+  L.part_lse = off;  off = align_up(off + sizeof(float) * (size_t)rows_cap);
+  L.part_o = off;    off = align_up(off + sizeof(float) * (size_t)rows_cap * kVdim);
+  L.total = off;
+  return L;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+}  // namespace
+
+struct mlaverify_handle {
+  mlaverify_config cfg;
+  int device;
+  char* ws;
+  size_t ws_bytes;
+  bool owns_ws;
+  Layout L;
+  int last_batch;
+  std::vector<hipEvent_t> prof_events;  // 4 per profiled run
+  int prof_max = 0, prof_runs = 0;
+};
+
+namespace {
+void release_profile(mlaverify_handle* hd) {
+  for (hipEvent_t e : hd->prof_events) (void)hipEventDestroy(e);
+  hd->prof_events.clear();
+  hd->prof_max = hd->prof_runs = 0;
+}
+}  // namespace
+
+extern "C" {
+
+int mlaverify_validate_config(const mlaverify_config* c) {
+  if (!c) return MLAVERIFY_ERR_INVALID_ARG;
+  if (c->max_tree_nodes > kMaxTree) return MLAVERIFY_ERR_UNSUPPORTED;
+  if (c->num_heads < 1 || c->num_heads > 128) return MLAVERIFY_ERR_INVALID_ARG;
+  if (c->max_batch < 1 || c->max_batch > kMaxBatch) return MLAVERIFY_ERR_INVALID_ARG;
+  if (c->max_tree_nodes < 1) return MLAVERIFY_ERR_INVALID_ARG;
+  if (c->max_prefix_len < 0 || c->max_prefix_len > (1 << 28)) return MLAVERIFY_ERR_INVALID_ARG;
+  if (c->pool_slots < 1 || c->pool_slots > INT32_MAX) return MLAVERIFY_ERR_INVALID_ARG;
+  if (c->kv_row_stride < kLatent || c->kv_row_stride % 8 != 0) return MLAVERIFY_ERR_INVALID_ARG;
+  if (!isfinite(c->sm_scale)) return MLAVERIFY_ERR_INVALID_ARG;
+  if (c->split_tokens < 0 || (c->split_tokens > 0 && c->split_tokens % kTileKeys != 0))
+    return MLAVERIFY_ERR_INVALID_ARG;
+  if (c->flags & ~(uint32_t)MLAVERIFY_FLAG_NO_FASTPATH) return MLAVERIFY_ERR_INVALID_ARG;
+  // key offsets and unit indices are 32-bit on the device
+  if ((int64_t)c->max_batch * ((int64_t)c->max_prefix_len + c->max_tree_nodes) > INT32_MAX)
+    return MLAVERIFY_ERR_UNSUPPORTED;
+  if (c->split_tokens > 0 && (int64_t)c->max_batch * cdiv(c->max_prefix_len > 0 ? c->max_prefix_len : 1, c->split_tokens) > (1 << 24))
+    return MLAVERIFY_ERR_UNSUPPORTED;
+  return MLAVERIFY_OK;
+}
+
+size_t mlaverify_workspace_bytes(const mlaverify_config* c) {
+  if (mlaverify_validate_config(c) != MLAVERIFY_OK) return 0;
+  return layout_for(*c).total;
+}
+
+int mlaverify_create(const mlaverify_config* c, void* workspace, size_t workspace_bytes, mlaverify_t* out) {
+  if (!out) return MLAVERIFY_ERR_INVALID_ARG;
+  *out = nullptr;
+  const int v = mlaverify_validate_config(c);
+  if (v != MLAVERIFY_OK) return v;
+  const Layout L = layout_for(*c);
+  if (workspace && workspace_bytes < L.total) return MLAVERIFY_ERR_WORKSPACE;
+  if (workspace && !aligned(workspace, kAlign)) return MLAVERIFY_ERR_INVALID_ARG;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MLAVERIFY_ERR_HIP;
+  mlaverify_handle* hd = new (std::nothrow) mlaverify_handle;
+  if (!hd) return MLAVERIFY_ERR_NO_MEMORY;
+  hd->cfg = *c;
+  hd->device = dev;
+  hd->L = L;
+  hd->last_batch = 0;
+  hd->owns_ws = (workspace == nullptr);
+  if (hd->owns_ws) {
+    void* p = nullptr;
+    if (hipMalloc(&p, L.total) != hipSuccess) {
+      delete hd;
+      return MLAVERIFY_ERR_NO_MEMORY;
+    }
+    hd->ws = static_cast<char*>(p);
+    hd->ws_bytes = L.total;
+  } else {
+    hd->ws = static_cast<char*>(workspace);
+    hd->ws_bytes = workspace_bytes;
+  }
+  // Clear the plan header (sticky error word) once; run never needs a memset.
+  if (hipMemset(hd->ws + L.hdr, 0, sizeof(PlanHeader)) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+    if (hd->owns_ws) (void)hipFree(hd->ws);
+    delete hd;
+    return MLAVERIFY_ERR_HIP;
+  }
+  *out = hd;
+  return MLAVERIFY_OK;
+}
+
+int mlaverify_run(mlaverify_t hd, int32_t batch, int32_t T, const void* q, const void* kv_pool,
+                  const int32_t* kv_indices, const int32_t* prefix_lens, const int32_t* tree_parent, void* out,
+                  float* lse, void* stream) {
+  if (!hd) return MLAVERIFY_ERR_INVALID_ARG;
+  const mlaverify_config& c = hd->cfg;
+  if (batch < 1 || batch > c.max_batch || T < 1 || T > c.max_tree_nodes) return MLAVERIFY_ERR_INVALID_ARG;
+  if (!q || !kv_pool || !kv_indices || !prefix_lens || !tree_parent || !out || !lse) return MLAVERIFY_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(kv_pool, 16) || !aligned(out, 16)) return MLAVERIFY_ERR_INVALID_ARG;
+  if (!aligned(kv_indices, 4) || !aligned(prefix_lens, 4) || !aligned(tree_parent, 4) || !aligned(lse, 4))
+    return MLAVERIFY_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Layout& L = hd->L;
+  const int n_mt = mtiles_for(c.num_heads, T);
+  const int units_grid = units_for(c, batch, T);
+  const int M = c.num_heads * T;
+
+  PlanArgs pa;
+  pa.prefix_lens = prefix_lens;
+  pa.tree_parent = tree_parent;
+  pa.hdr = reinterpret_cast<PlanHeader*>(hd->ws + L.hdr);
+  pa.req = reinterpret_cast<ReqPlan*>(hd->ws + L.req);
+  pa.unit_tab = reinterpret_cast<int32_t*>(hd->ws + L.unit_tab);
+  pa.masks = reinterpret_cast<uint64_t*>(hd->ws + L.masks);
+  pa.batch = batch;
+  pa.T = T;
+  pa.max_prefix = c.max_prefix_len;
+  pa.split_fixed = c.split_tokens;
+  pa.target_units = target_units_for(n_mt);
+  pa.min_split = kMinSplit;
+  pa.units_cap = units_grid;
+  pa.n_mtiles = n_mt;
+
+  PartialArgs ka;
+  ka.q = static_cast<const uint16_t*>(q);
+  ka.pool = static_cast<const uint16_t*>(kv_pool);
+  ka.kv_indices = kv_indices;
+  ka.hdr = pa.hdr;
+  ka.req = pa.req;
+  ka.unit_tab = pa.unit_tab;
+  ka.masks = pa.masks;
+  ka.part_o = reinterpret_cast<float*>(hd->ws + L.part_o);
+  ka.part_lse = reinterpret_cast<float*>(hd->ws + L.part_lse);
+  ka.sticky_err = &pa.hdr->sticky_err;
+  ka.req_rw = pa.req;
+  ka.pool_slots = c.pool_slots;
+  ka.row_stride_bytes = c.kv_row_stride * 2;
+  ka.T = T;
+  ka.H = c.num_heads;
+  ka.M = M;
+  ka.n_mtiles = n_mt;
+  ka.scale_log2 = c.sm_scale * 1.4426950408889634f;
+  ka.flags = c.flags;
+
+  MergeArgs ma;
+  ma.req = pa.req;
+  ma.part_o = ka.part_o;
+  ma.part_lse = ka.part_lse;
+  ma.out = static_cast<uint16_t*>(out);
+  ma.lse = lse;
+  ma.batch = batch;
+  ma.M = M;
+
+  const int grid = n_mt * (int)(cdiv(units_grid, 8) * 8);
+  hipEvent_t* ev = nullptr;
+  if (hd->prof_runs < hd->prof_max) ev = &hd->prof_events[4 * hd->prof_runs++];
+  if (ev && hipEventRecord(ev[0], s) != hipSuccess) return MLAVERIFY_ERR_HIP;
+  if (launch_plan(pa, s) != hipSuccess) return MLAVERIFY_ERR_HIP;
+  if (ev && hipEventRecord(ev[1], s) != hipSuccess) return MLAVERIFY_ERR_HIP;
+  if (launch_partial(ka, grid, s) != hipSuccess) return MLAVERIFY_ERR_HIP;
+  if (ev && hipEventRecord(ev[2], s) != hipSuccess) return MLAVERIFY_ERR_HIP;
+  if (launch_merge(ma, s) != hipSuccess) return MLAVERIFY_ERR_HIP;
+  if (ev && hipEventRecord(ev[3], s) != hipSuccess) return MLAVERIFY_ERR_HIP;
+  hd->last_batch = batch;
+  return MLAVERIFY_OK;
+}
+
+int mlaverify_tree_masks(const int32_t* tree_parent, int32_t batch, int32_t T, uint64_t* masks, uint32_t* err,
+                         void* stream) {
+  if (!tree_parent || !masks || !err || batch < 1 || T < 1) return MLAVERIFY_ERR_INVALID_ARG;
+  if (T > kMaxTree) return MLAVERIFY_ERR_UNSUPPORTED;
+  if (batch > (1 << 24)) return MLAVERIFY_ERR_INVALID_ARG;
+  if (!aligned(tree_parent, 4) || !aligned(masks, 8) || !aligned(err, 4)) return MLAVERIFY_ERR_INVALID_ARG;
+  if (launch_tree_masks(tree_parent, batch, T, masks, err, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return MLAVERIFY_ERR_HIP;
+  return MLAVERIFY_OK;
+}
+
+int mlaverify_read_plan(mlaverify_t hd, int32_t batch, void* stream, int32_t* host_out, int32_t capacity) {
+  if (!hd || batch < 1 || batch > hd->cfg.max_batch || (capacity > 0 && !host_out) || capacity < 0)
+    return MLAVERIFY_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int needed = 3 + 5 * batch;
+  PlanHeader hdr;
+  ReqPlan* req = new (std::nothrow) ReqPlan[batch];
+  if (!req) return MLAVERIFY_ERR_NO_MEMORY;
+  bool ok = hipMemcpyAsync(&hdr, hd->ws + hd->L.hdr, sizeof(hdr), hipMemcpyDeviceToHost, s) == hipSuccess &&
+            hipMemcpyAsync(req, hd->ws + hd->L.req, sizeof(ReqPlan) * batch, hipMemcpyDeviceToHost, s) == hipSuccess &&
+            hipStreamSynchronize(s) == hipSuccess;
+  if (!ok) {
+    delete[] req;
+    return MLAVERIFY_ERR_HIP;
+  }
+  int32_t vals[3] = {hdr.split_len, hdr.total_units, hdr.n_mtiles};
+  for (int i = 0; i < 3 && i < capacity; i++) host_out[i] = vals[i];
+  for (int b = 0; b < batch; b++) {
+    const int32_t rv[5] = {req[b].key_off, req[b].prefix_len, req[b].first_unit, req[b].units, (int32_t)req[b].err};
+    for (int k = 0; k < 5; k++) {
+      const int pos = 3 + 5 * b + k;
+      if (pos < capacity) host_out[pos] = rv[k];
+    }
+  }
+  delete[] req;
+  return needed;
+}
+
+int mlaverify_read_device_errors(mlaverify_t hd, void* stream, uint32_t* flags) {
+  if (!hd || !flags) return MLAVERIFY_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint32_t v = 0;
+  char* p = hd->ws + hd->L.hdr + offsetof(PlanHeader, sticky_err);
+  if (hipMemcpyAsync(&v, p, sizeof(v), hipMemcpyDeviceToHost, s) != hipSuccess) return MLAVERIFY_ERR_HIP;
+  if (hipMemsetAsync(p, 0, sizeof(v), s) != hipSuccess) return MLAVERIFY_ERR_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return MLAVERIFY_ERR_HIP;
+  *flags = v;
+  return MLAVERIFY_OK;
+}
+
+int mlaverify_profile_begin(mlaverify_t hd, int32_t max_runs) {
+  if (!hd || max_runs < 1 || max_runs > (1 << 20)) return MLAVERIFY_ERR_INVALID_ARG;
+  release_profile(hd);
+  hd->prof_events.resize(4 * (size_t)max_runs);
+  for (size_t i = 0; i < hd->prof_events.size(); i++) {
+    if (hipEventCreate(&hd->prof_events[i]) != hipSuccess) {
+      hd->prof_events.resize(i);
+      release_profile(hd);
+      return MLAVERIFY_ERR_HIP;
+    }
+  }
+  hd->prof_max = max_runs;
+  hd->prof_runs = 0;
+  return MLAVERIFY_OK;
+}
+
+int mlaverify_profile_end(mlaverify_t hd, float* host_ms, int32_t capacity_runs) {
+  if (!hd || capacity_runs < 0 || (capacity_runs > 0 && !host_ms)) return MLAVERIFY_ERR_INVALID_ARG;
+  const int runs = hd->prof_runs;
+  int rc = runs;
+  if (runs > 0 && hipEventSynchronize(hd->prof_events[4 * runs - 1]) != hipSuccess) rc = MLAVERIFY_ERR_HIP;
+  for (int i = 0; rc >= 0 && i < runs && i < capacity_runs; i++)
+    for (int k = 0; k < 3; k++)
+      if (hipEventElapsedTime(&host_ms[3 * i + k], hd->prof_events[4 * i + k], hd->prof_events[4 * i + k + 1]) !=
+          hipSuccess)
+        rc = MLAVERIFY_ERR_HIP;
+  release_profile(hd);
+  return rc;
+}
+
+int mlaverify_destroy(mlaverify_t hd) {
+  if (!hd) return MLAVERIFY_ERR_INVALID_ARG;
+  release_profile(hd);
+  if (hd->owns_ws && hd->ws) (void)hipFree(hd->ws);
+  delete hd;
+  return MLAVERIFY_OK;
+}
+
+const char* mlaverify_status_string(int status) {
+  switch (status) {
+    case MLAVERIFY_OK: return "ok";
+    case MLAVERIFY_ERR_INVALID_ARG: return "invalid argument";
+    case MLAVERIFY_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MLAVERIFY_ERR_NO_MEMORY: return "out of memory";
+    case MLAVERIFY_ERR_WORKSPACE: return "workspace too small";
+    case MLAVERIFY_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

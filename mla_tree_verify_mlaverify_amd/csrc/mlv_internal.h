@@ -1,0 +1,97 @@
+// Internal layout shared by the host library and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mlv {
+
+constexpr int kLatent = 576;          // score columns of a latent KV row (512 latent + 64 rope)
+constexpr int kVdim = 512;            // value columns (leading part of the same row)
+constexpr int kRowBytes = kLatent * 2;
+constexpr int kChunksPerRow = kRowBytes / 16;  // 72 sixteen-byte chunks per row
+constexpr int kTileKeys = 32;          // keys per LDS tile
+constexpr int kTileBytes = kTileKeys * kRowBytes;  // 36864
+constexpr int kRowsPerWave = 32;       // query rows (head x node) held by one wave
+constexpr int kWaves = 4;
+constexpr int kRowsPerBlock = kRowsPerWave * kWaves;  // 128 rows per workgroup (M tile)
+constexpr int kThreads = 64 * kWaves;
+constexpr int kQReg = 20;                               // Q k-steps (16 columns each) kept in VGPRs
+constexpr int kQLdsBytes = (36 - kQReg) * 64 * 16;      // per-wave LDS slice for the other k-steps
+constexpr int kMaxTree = 64;
+constexpr int kMaxBatch = 1024;        // one plan thread per request
+constexpr int kTargetBlocks = 256;     // workgroups the split aims for (one per CU on MI355X)
+constexpr int kMinSplit = 128;         // shortest automatic prefix split, in tokens
+constexpr int kPlanThreads = 1024;
+
+// Device-side error bits (mirrors MLAVERIFY_DEVERR_* in the public header).
+constexpr uint32_t kErrBadParent = 0x1u;
+constexpr uint32_t kErrBadIndex = 0x2u;
+constexpr uint32_t kErrBadPrefix = 0x4u;
+
+struct PlanHeader {
+  int32_t split_len;     // prefix tokens per split unit
+  int32_t total_units;   // units in use by this run
+  int32_t n_mtiles;      // 128-row tiles per request
+  int32_t pad0;
+  uint32_t sticky_err;   // OR of every data error since the last readback
+  uint32_t pad1[59];     // header is 256 bytes
+};
+static_assert(sizeof(PlanHeader) == 256, "header size");
+
+struct ReqPlan {
+  int32_t key_off;      // start of the request's segment in kv_indices
+  int32_t prefix_len;   // P_b after validation (0 when invalid)
+  int32_t first_unit;   // global index of its first split unit
+  int32_t units;        // number of split units (the last one also covers the tree)
+  uint32_t err;         // data-error bits of this request
+  int32_t pad[3];
+};
+static_assert(sizeof(ReqPlan) == 32, "ReqPlan size");
+
+struct PlanArgs {
+  const int32_t* prefix_lens;
+  const int32_t* tree_parent;
+  PlanHeader* hdr;
+  ReqPlan* req;
+  int32_t* unit_tab;     // unit -> request
+  uint64_t* masks;       // [batch, T] ancestor-or-self bitmasks
+  int32_t batch, T, max_prefix, split_fixed, target_units, min_split, units_cap, n_mtiles;
+};
+
+struct PartialArgs {
+  const uint16_t* q;
+  const uint16_t* pool;
+  const int32_t* kv_indices;
+  const PlanHeader* hdr;
+  const ReqPlan* req;
+  const int32_t* unit_tab;
+  const uint64_t* masks;
+  float* part_o;         // [units, M, 512] unit-normalised partial outputs
+  float* part_lse;       // [units, M] log2-domain lse of each partial
+  uint32_t* sticky_err;
+  ReqPlan* req_rw;       // for index-error reporting
+  int64_t pool_slots;
+  int64_t row_stride_bytes;
+  int32_t T, H, M, n_mtiles;
+  float scale_log2;      // sm_scale * log2(e)
+  uint32_t flags;
+};
+
+struct MergeArgs {
+  const ReqPlan* req;
+  const float* part_o;
+  const float* part_lse;
+  uint16_t* out;
+  float* lse;
+  int32_t batch, M;
+};
+
+// Launchers (kernels.hip).
+hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
+hipError_t launch_partial(const PartialArgs& a, int grid, hipStream_t s);
+hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
+hipError_t launch_tree_masks(const int32_t* tree_parent, int batch, int T, uint64_t* masks, uint32_t* err,
+                             hipStream_t s);
+
+}  // namespace mlv

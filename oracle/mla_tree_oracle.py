@@ -135,7 +135,7 @@ def attention_over_slots(q_rows, pool, slots, sm_scale: float):
 
 
 def verify_attention(q, pool, kv_indices, prefix_lens, tree_parent, sm_scale: float,
-                     *, nodes_per_chunk: int = 16):
+                     *, nodes_per_chunk: int = 16, nodes=None):
     """Tree-verify attention for a batch, in float64.
 
     q: uint16 bf16 bits [B*T, H, 576]; pool: uint16 [slots, row_stride >= 576];
@@ -147,6 +147,9 @@ def verify_attention(q, pool, kv_indices, prefix_lens, tree_parent, sm_scale: fl
     definition evaluated for several rows at once); the ancestor keys of each node
     are then appended to that node's score list, and softmax, lse and the weighted
     sum of V rows follow the definition row by row.
+
+    ``nodes``: optional iterable of (b, i) pairs; only those rows are computed and
+    every other row of the result is NaN (for sampled checks of large batches).
     """
     q = np.asarray(q)
     pool = np.asarray(pool)
@@ -161,23 +164,28 @@ def verify_attention(q, pool, kv_indices, prefix_lens, tree_parent, sm_scale: fl
     if np.any(prefix_lens < 0):
         raise ValueError("negative prefix length")
     offs = request_offsets(prefix_lens, t)
-    out = np.zeros((bsz * t, h, VDIM))
-    lse = np.zeros((bsz * t, h))
+    fill = 0.0 if nodes is None else np.nan
+    out = np.full((bsz * t, h, VDIM), fill)
+    lse = np.full((bsz * t, h), fill)
+    wanted = None if nodes is None else {(int(b), int(i)) for b, i in nodes}
     for b in range(bsz):
         validate_parents(tree_parent[b])
+        if wanted is not None and not any(bb == b for bb, _ in wanted):
+            continue
         p = int(prefix_lens[b])
         seg = kv_indices[offs[b]:offs[b] + p + t].astype(np.int64)
         k_pre = bf16_to_f64(pool[seg[:p], :LATENT])  # [P, 576]
         k_tree = bf16_to_f64(pool[seg[p:], :LATENT])  # [T, 576]
-        for n0 in range(0, t, nodes_per_chunk):
-            n1 = min(t, n0 + nodes_per_chunk)
-            qb = bf16_to_f64(q[b * t + n0:b * t + n1])  # [n, H, 576]
+        sel = list(range(t)) if wanted is None else sorted(i for bb, i in wanted if bb == b)
+        for c0 in range(0, len(sel), nodes_per_chunk):
+            chunk = sel[c0:c0 + nodes_per_chunk]
+            qb = bf16_to_f64(q[b * t + np.asarray(chunk)])  # [n, H, 576]
             s_pre = sm_scale * (qb.reshape(-1, LATENT) @ k_pre.T)  # [n*H, P]
-            s_pre = s_pre.reshape(n1 - n0, h, p)
-            for i in range(n0, n1):
+            s_pre = s_pre.reshape(len(chunk), h, p)
+            for ci, i in enumerate(chunk):
                 anc = np.asarray(ancestors_with_self(tree_parent[b, :], i), dtype=np.int64)
                 k_anc = k_tree[anc]  # [a, 576]
-                s = np.concatenate([s_pre[i - n0], sm_scale * (qb[i - n0] @ k_anc.T)], axis=1)
+                s = np.concatenate([s_pre[ci], sm_scale * (qb[ci] @ k_anc.T)], axis=1)
                 m = s.max(axis=1, keepdims=True)
                 e = np.exp(s - m)
                 z = e.sum(axis=1, keepdims=True)

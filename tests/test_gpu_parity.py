@@ -1,0 +1,243 @@
+"""GPU parity of the HIP verify path against the CPU fp64 oracle, through the C ABI.
+
+Sizes span several 32-key tiles, split units and 128-row M tiles with ragged tails;
+the workload configs run at full size.  Bitwise identities (fast path on/off,
+permuted pool, repeat runs, poisoned unused rows / workspace) need no tolerance.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import mla_tree_verify_mlaverify_amd as mv
+from gpu_util import DEV, compare, i32, run_gpu, run_oracle, upload, verifier_for
+from oracle import mla_tree_oracle as orc
+from workloads import synth
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+# --------------------------------------------------------------------------- a.1 masks
+
+@pytest.mark.parametrize("seed", range(4))
+def test_tree_masks_bit_exact(seed):
+    rng = np.random.default_rng(seed)
+    for t in (1, 2, 7, 8, 31, 32, 33, 63, 64):
+        trees = [synth.random_tree(rng, t), synth.chain_tree(t),
+                 np.array([int(rng.integers(-1, i)) for i in range(t)], dtype=np.int32)]
+        par = np.stack(trees).astype(np.int32)
+        masks, err = mv.tree_masks(i32(par))
+        torch.cuda.synchronize()
+        got = masks.cpu().numpy().view(np.uint64)
+        for b in range(len(trees)):
+            assert np.array_equal(got[b], orc.ancestor_masks(par[b])), (t, b)
+        assert np.all(err.cpu().numpy() == 0)
+
+
+def test_tree_masks_flag_bad_parents():
+    par = np.array([[-1, 0, 1, 2], [-1, 0, 2, 1], [-1, 5, 0, 0], [0, -1, 1, 1], [-1, -2, 0, 0]], dtype=np.int32)
+    masks, err = mv.tree_masks(i32(par))
+    torch.cuda.synchronize()
+    e = err.cpu().numpy()
+    m = masks.cpu().numpy().view(np.uint64)
+    assert e.tolist() == [0, mv.DEVERR_BAD_PARENT, mv.DEVERR_BAD_PARENT, mv.DEVERR_BAD_PARENT, mv.DEVERR_BAD_PARENT]
+    assert np.array_equal(m[0], orc.ancestor_masks(par[0]))
+    assert np.all(m[1:] == 0)
+
+
+# --------------------------------------------------------------------------- small parity
+
+SMALL = [
+    # seed, prefix per request, T, H, tree kind, split_tokens
+    (0, [0], 1, 1, "random", 0),
+    (1, [1], 1, 8, "random", 0),
+    (2, [31, 33], 5, 8, "random", 0),
+    (3, [100, 0, 257], 8, 8, "forest", 32),
+    (4, [300], 32, 8, "random", 64),
+    (5, [129, 64], 33, 4, "chain", 0),
+    (6, [1000], 64, 8, "random", 0),
+    (7, [513, 77, 0, 1], 17, 16, "forest", 96),
+    (8, [2047], 64, 3, "random", 128),
+    (9, [640, 641], 64, 2, "random", 0),
+]
+
+
+@pytest.mark.parametrize("seed,prefix,t,h,tree,split", SMALL)
+def test_small_parity(seed, prefix, t, h, tree, split):
+    cfg = synth.small_config(seed, batch=len(prefix), prefix=prefix, tree_nodes=t, heads=h,
+                             slots=max(4096, 2 * (sum(prefix) + len(prefix) * t)), tree=tree, q_scale=1.0)
+    out, lse, v = run_gpu(cfg, split_tokens=split)
+    ref_out, ref_lse = run_oracle(cfg)
+    compare(out, lse, ref_out, ref_lse)
+    plan = v.read_plan()
+    # the unit partition covers each prefix exactly once, in split_len pieces
+    offs = orc.request_offsets(cfg["prefix_lens"], t)
+    first = 0
+    for b, rq in enumerate(plan["requests"]):
+        assert rq["key_offset"] == offs[b] and rq["prefix_len"] == prefix[b]
+        assert rq["first_unit"] == first and rq["units"] == max(1, math.ceil(prefix[b] / plan["split_len"]))
+        first += rq["units"]
+        assert rq["error_bits"] == 0
+    assert plan["total_units"] == first
+    if split:
+        assert plan["split_len"] == split
+
+
+# --------------------------------------------------------------------------- workload configs
+
+@pytest.mark.parametrize("i", [0, 1, 2, 5, 6])
+def test_config_parity_full(i):
+    cfg = synth.make_config(i)
+    out, lse, _ = run_gpu(cfg)
+    ref_out, ref_lse = run_oracle(cfg)
+    print(i, compare(out, lse, ref_out, ref_lse))
+
+
+@pytest.mark.parametrize("i", [3, 4])
+def test_config_parity_sampled(i):
+    cfg = synth.make_config(i)
+    out, lse, _ = run_gpu(cfg)
+    rng = np.random.default_rng(100 + i)
+    t = cfg["tree_nodes"]
+    nodes = [(b, n) for b in range(cfg["batch"]) for n in sorted({0, t - 1, *rng.integers(0, t, 6).tolist()})]
+    ref_out, ref_lse = run_oracle(cfg, nodes=nodes)
+    print(i, compare(out, lse, ref_out, ref_lse))
+
+
+# --------------------------------------------------------------------------- sensitive variants
+
+@pytest.mark.parametrize("variant", ["sorted", "contiguous", "sharp", "needle_prefix", "needle_tree", "prefix0",
+                                     "chain"])
+def test_variant_parity(variant):
+    cfg = synth.make_config(1, variant=variant)
+    out, lse, _ = run_gpu(cfg)
+    ref_out, ref_lse = run_oracle(cfg)
+    compare(out, lse, ref_out, ref_lse)
+    if variant.startswith("needle"):
+        assert np.abs(ref_out).max() > 1.0  # the needle dominates somewhere
+
+
+def test_q_zero_lse_is_log_count():
+    cfg = synth.make_config(0, variant="qzero")
+    out, lse, _ = run_gpu(cfg)
+    g = [257, 258, 259, 260, 258, 259, 259, 260]
+    np.testing.assert_allclose(lse, np.log(np.array(g, dtype=np.float64))[:, None].repeat(8, 1), atol=2e-6)
+    ref_out, ref_lse = run_oracle(cfg)
+    compare(out, lse, ref_out, ref_lse)
+
+
+def test_row_stride_larger_than_row():
+    cfg = synth.small_config(21, batch=2, prefix=[300, 45], tree_nodes=9, heads=8, slots=2048, row_stride=640)
+    out, lse, _ = run_gpu(cfg)
+    ref_out, ref_lse = run_oracle(cfg)
+    compare(out, lse, ref_out, ref_lse)  # the NaN padding columns are never read
+
+
+# --------------------------------------------------------------------------- bitwise identities
+
+def test_fast_path_is_bit_identical():
+    cfg = synth.make_config(1, variant="contiguous")
+    a, la, _ = run_gpu(cfg)
+    b, lb, _ = run_gpu(cfg, flags=mv.FLAG_NO_FASTPATH)
+    assert np.array_equal(a, b) and np.array_equal(la, lb)
+
+
+def test_permuted_pool_is_bit_identical():
+    cfg = synth.make_config(1)
+    perm = synth.permute_pool(cfg, np.random.default_rng(7))
+    a, la, _ = run_gpu(cfg)
+    b, lb, _ = run_gpu(perm)
+    assert np.array_equal(a, b) and np.array_equal(la, lb)
+
+
+def test_repeat_runs_are_bit_identical():
+    cfg = synth.make_config(2)
+    d = upload(cfg)
+    v = verifier_for(cfg)
+    a, la, _ = run_gpu(cfg, v, d)
+    b, lb, _ = run_gpu(cfg, v, d)
+    assert np.array_equal(a, b) and np.array_equal(la, lb)
+
+
+def test_poisoned_unused_rows_do_not_change_output():
+    cfg = synth.make_config(1)
+    a, la, _ = run_gpu(cfg)
+    b, lb, _ = run_gpu(synth.apply_variant(cfg, "poison_unused"))
+    assert np.array_equal(a, b) and np.array_equal(la, lb)
+
+
+def test_poisoned_workspace_does_not_change_output():
+    cfg = synth.small_config(22, batch=3, prefix=[700, 5, 1500], tree_nodes=24, heads=8, slots=8192)
+    d = upload(cfg)
+    v = verifier_for(cfg)
+    a, la, _ = run_gpu(cfg, v, d)
+    v.workspace.fill_(0xFF)  # NaN in every float of the workspace
+    torch.cuda.synchronize()
+    b, lb, _ = run_gpu(cfg, v, d)
+    assert np.array_equal(a, b) and np.array_equal(la, lb)
+
+
+@pytest.mark.parametrize("split", [32, 64, 256, 1024, 4096])
+def test_split_length_changes_only_rounding(split):
+    cfg = synth.make_config(1)
+    out, lse, v = run_gpu(cfg, split_tokens=split)
+    assert v.read_plan()["split_len"] == split
+    ref_out, ref_lse = run_oracle(cfg)
+    compare(out, lse, ref_out, ref_lse)
+
+
+# --------------------------------------------------------------------------- errors
+
+def test_device_errors_poison_only_the_offending_request():
+    cfg = synth.small_config(30, batch=4, prefix=[200, 300, 100, 50], tree_nodes=12, heads=8, slots=4096)
+    bad = dict(cfg)
+    par = cfg["tree_parent"].copy()
+    par[1, 5] = 7  # parent after the node
+    idx = cfg["kv_indices"].copy()
+    idx[200 + 12 + 300 + 12 + 17] = 4096 + 3  # request 2, prefix slot 17: outside the pool
+    plens = cfg["prefix_lens"].copy()
+    bad.update(tree_parent=par, kv_indices=idx)
+    v = verifier_for(cfg, max_prefix=300)
+    out, lse, _ = run_gpu(bad, v)
+    flags = v.read_device_errors()
+    assert flags == mv.DEVERR_BAD_PARENT | mv.DEVERR_BAD_INDEX
+    assert v.read_device_errors() == 0  # read clears
+    t = 12
+    ref_out, ref_lse = run_oracle(cfg)
+    for b in range(4):
+        rows = slice(b * t, (b + 1) * t)
+        if b in (1, 2):
+            assert np.all(np.isnan(out[rows])) and np.all(np.isnan(lse[rows]))
+        else:
+            compare(out[rows], lse[rows], ref_out[rows], ref_lse[rows])
+    # prefix longer than max_prefix_len
+    plens[3] = 301
+    bad2 = synth.small_config(30, batch=4, prefix=list(plens), tree_nodes=12, heads=8, slots=4096)
+    out2, lse2, _ = run_gpu(bad2, v)
+    assert v.read_device_errors() == mv.DEVERR_BAD_PREFIX
+    assert np.all(np.isnan(out2[3 * t:])) and np.all(np.isfinite(out2[:3 * t]))
+
+
+def test_host_argument_errors_enqueue_nothing():
+    cfg = synth.make_config(0)
+    v = verifier_for(cfg)
+    d = upload(cfg)
+    out = torch.full((8, 8, 512), 7.0, dtype=torch.bfloat16, device=DEV)
+    lse = torch.full((8, 8), 7.0, dtype=torch.float32, device=DEV)
+    lib = v.lib
+    import ctypes
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    args = [d["q"].data_ptr(), d["pool"].data_ptr(), d["kv_indices"].data_ptr(), d["prefix_lens"].data_ptr(),
+            d["tree_parent"].data_ptr(), out.data_ptr(), lse.data_ptr(), s]
+    assert lib.mlaverify_run(v.handle, 2, 8, *args) == mv.binding.ERR_INVALID_ARG  # batch > max_batch
+    assert lib.mlaverify_run(v.handle, 1, 9, *args) == mv.binding.ERR_INVALID_ARG  # T > max_tree_nodes
+    bad = list(args)
+    bad[0] = d["q"].data_ptr() + 2  # misaligned q
+    assert lib.mlaverify_run(v.handle, 1, 8, *bad) == mv.binding.ERR_INVALID_ARG
+    bad = list(args)
+    bad[5] = 0
+    assert lib.mlaverify_run(v.handle, 1, 8, *bad) == mv.binding.ERR_INVALID_ARG
+    torch.cuda.synchronize()
+    assert torch.all(out.float() == 7.0) and torch.all(lse == 7.0)
