@@ -78,7 +78,7 @@ typedef struct mlaverify_config {
   int32_t max_prefix_len;  /* largest P_b accepted; larger ones are device errors */
   int64_t pool_slots;      /* rows in kv_pool; indices outside [0, pool_slots) are device errors */
   int64_t kv_row_stride;   /* elements between consecutive pool rows, >= 576, multiple of 8 */
-  float sm_scale;          /* softmax scale sigma (e.g. 1/sqrt(192)) */
+  float sm_scale;          /* softmax scale sigma > 0 (e.g. 1/sqrt(192)) */
   int32_t split_tokens;    /* 0: choose the prefix split length per call on the device;
                               else a fixed split length in tokens, a multiple of 32 */
   uint32_t flags;          /* MLAVERIFY_FLAG_* */
@@ -133,7 +133,8 @@ MLAVERIFY_API int mlaverify_tree_masks(const int32_t* tree_parent, int32_t batch
 /* Copies the work partition of the most recent run into host memory (synchronises
  * `stream`; for tests and reports, not for graphs).  Writes up to `capacity`
  * int32 values: [split_len, total_units, n_mtiles, then per request b:
- * key_offset_b, prefix_len_b, first_unit_b, units_b, error_bits_b].
+ * key_offset_b, prefix_len_b, first_unit_b, units_b, prefix_error_bits_b]
+ * (parent and index errors are reported by mlaverify_read_device_errors only).
  * Returns the number of values available (which may exceed capacity) or a
  * negative status. */
 MLAVERIFY_API int mlaverify_read_plan(mlaverify_t h, int32_t batch, void* stream, int32_t* host_out,
@@ -144,9 +145,9 @@ MLAVERIFY_API int mlaverify_read_device_errors(mlaverify_t h, void* stream, uint
 
 /* Kernel timing for benchmarks (not for graph capture).  After
  * mlaverify_profile_begin(h, n) the next n calls of mlaverify_run record HIP events
- * on their stream before and after each of their three kernels (plan, partial,
- * merge).  mlaverify_profile_end synchronises on the last event, writes
- * host_ms[3*i + k] = duration in milliseconds of kernel k of recorded run i for
+ * on their stream before and after each of their two kernels (partial pass, merge).
+ * mlaverify_profile_end synchronises on the last event, writes host_ms[2*i + k] =
+ * duration in milliseconds of kernel k of recorded run i for
  * i < min(runs, capacity_runs), releases the events and returns the number of runs
  * recorded (or a negative status).  begin while a session is open restarts it. */
 MLAVERIFY_API int mlaverify_profile_begin(mlaverify_t h, int32_t max_runs);

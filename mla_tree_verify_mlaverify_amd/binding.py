@@ -15,7 +15,8 @@ import os
 import torch
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG_DIR, "libmlaverify.so")
+# MLAVERIFY_LIBRARY may name another build of the same library (e.g. for A/B timing).
+LIB_PATH = os.environ.get("MLAVERIFY_LIBRARY") or os.path.join(_PKG_DIR, "libmlaverify.so")
 
 LATENT_DIM = 576
 V_DIM = 512
@@ -242,13 +243,13 @@ class Verifier:
         self._prof_cap = max_runs
 
     def profile_end(self):
-        """Per recorded run: (plan_ms, partial_ms, merge_ms); synchronises."""
+        """Per recorded run: (partial_ms, merge_ms); synchronises."""
         cap = getattr(self, "_prof_cap", 0)
-        buf = (ctypes.c_float * (3 * max(cap, 1)))()
+        buf = (ctypes.c_float * (2 * max(cap, 1)))()
         n = self.lib.mlaverify_profile_end(self.handle, buf, cap)
         if n < 0:
             raise MlaVerifyError(n, "mlaverify_profile_end")
-        return [tuple(buf[3 * i:3 * i + 3]) for i in range(min(n, cap))]
+        return [tuple(buf[2 * i:2 * i + 2]) for i in range(min(n, cap))]
 
     def read_device_errors(self, stream=None) -> int:
         """Sticky device-side data-error bits since the last call (synchronises the stream)."""

@@ -70,7 +70,7 @@ struct mlaverify_handle {
   bool owns_ws;
   Layout L;
   int last_batch;
-  std::vector<hipEvent_t> prof_events;  // 4 per profiled run
+  std::vector<hipEvent_t> prof_events;  // 3 per profiled run
   int prof_max = 0, prof_runs = 0;
 };
 
@@ -93,7 +93,7 @@ int mlaverify_validate_config(const mlaverify_config* c) {
   if (c->max_prefix_len < 0 || c->max_prefix_len > (1 << 28)) return MLAVERIFY_ERR_INVALID_ARG;
   if (c->pool_slots < 1 || c->pool_slots > INT32_MAX) return MLAVERIFY_ERR_INVALID_ARG;
   if (c->kv_row_stride < kLatent || c->kv_row_stride % 8 != 0) return MLAVERIFY_ERR_INVALID_ARG;
-  if (!isfinite(c->sm_scale)) return MLAVERIFY_ERR_INVALID_ARG;
+  if (!isfinite(c->sm_scale) || !(c->sm_scale > 0.f)) return MLAVERIFY_ERR_INVALID_ARG;
   if (c->split_tokens < 0 || (c->split_tokens > 0 && c->split_tokens % kTileKeys != 0))
     return MLAVERIFY_ERR_INVALID_ARG;
   if (c->flags & ~(uint32_t)MLAVERIFY_FLAG_NO_FASTPATH) return MLAVERIFY_ERR_INVALID_ARG;
@@ -165,62 +165,50 @@ int mlaverify_run(mlaverify_t hd, int32_t batch, int32_t T, const void* q, const
   const int units_grid = units_for(c, batch, T);
   const int M = c.num_heads * T;
 
-  PlanArgs pa;
-  pa.prefix_lens = prefix_lens;
-  pa.tree_parent = tree_parent;
-  pa.hdr = reinterpret_cast<PlanHeader*>(hd->ws + L.hdr);
-  pa.req = reinterpret_cast<ReqPlan*>(hd->ws + L.req);
-  pa.unit_tab = reinterpret_cast<int32_t*>(hd->ws + L.unit_tab);
-  pa.masks = reinterpret_cast<uint64_t*>(hd->ws + L.masks);
-  pa.batch = batch;
-  pa.T = T;
-  pa.max_prefix = c.max_prefix_len;
-  pa.split_fixed = c.split_tokens;
-  pa.target_units = target_units_for(n_mt);
-  pa.min_split = kMinSplit;
-  pa.units_cap = units_grid;
-  pa.n_mtiles = n_mt;
-
   PartialArgs ka;
   ka.q = static_cast<const uint16_t*>(q);
   ka.pool = static_cast<const uint16_t*>(kv_pool);
   ka.kv_indices = kv_indices;
-  ka.hdr = pa.hdr;
-  ka.req = pa.req;
-  ka.unit_tab = pa.unit_tab;
-  ka.masks = pa.masks;
+  ka.prefix_lens = prefix_lens;
+  ka.tree_parent = tree_parent;
+  ka.hdr = reinterpret_cast<PlanHeader*>(hd->ws + L.hdr);
+  ka.req = reinterpret_cast<ReqPlan*>(hd->ws + L.req);
   ka.part_o = reinterpret_cast<float*>(hd->ws + L.part_o);
   ka.part_lse = reinterpret_cast<float*>(hd->ws + L.part_lse);
-  ka.sticky_err = &pa.hdr->sticky_err;
-  ka.req_rw = pa.req;
+  ka.sticky_err = &ka.hdr->sticky_err;
   ka.pool_slots = c.pool_slots;
   ka.row_stride_bytes = c.kv_row_stride * 2;
+  ka.batch = batch;
   ka.T = T;
   ka.H = c.num_heads;
   ka.M = M;
   ka.n_mtiles = n_mt;
+  ka.max_prefix = c.max_prefix_len;
+  ka.split_fixed = c.split_tokens;
+  ka.target_units = target_units_for(n_mt);
+  ka.min_split = kMinSplit;
+  ka.units_cap = units_grid;
   ka.scale_log2 = c.sm_scale * 1.4426950408889634f;
   ka.flags = c.flags;
 
   MergeArgs ma;
-  ma.req = pa.req;
+  ma.req = ka.req;
   ma.part_o = ka.part_o;
   ma.part_lse = ka.part_lse;
   ma.out = static_cast<uint16_t*>(out);
   ma.lse = lse;
   ma.batch = batch;
   ma.M = M;
+  ma.units_cap = units_grid;
 
   const int grid = n_mt * (int)(cdiv(units_grid, 8) * 8);
   hipEvent_t* ev = nullptr;
-  if (hd->prof_runs < hd->prof_max) ev = &hd->prof_events[4 * hd->prof_runs++];
+  if (hd->prof_runs < hd->prof_max) ev = &hd->prof_events[3 * hd->prof_runs++];
   if (ev && hipEventRecord(ev[0], s) != hipSuccess) return MLAVERIFY_ERR_HIP;
-  if (launch_plan(pa, s) != hipSuccess) return MLAVERIFY_ERR_HIP;
-  if (ev && hipEventRecord(ev[1], s) != hipSuccess) return MLAVERIFY_ERR_HIP;
   if (launch_partial(ka, grid, s) != hipSuccess) return MLAVERIFY_ERR_HIP;
-  if (ev && hipEventRecord(ev[2], s) != hipSuccess) return MLAVERIFY_ERR_HIP;
+  if (ev && hipEventRecord(ev[1], s) != hipSuccess) return MLAVERIFY_ERR_HIP;
   if (launch_merge(ma, s) != hipSuccess) return MLAVERIFY_ERR_HIP;
-  if (ev && hipEventRecord(ev[3], s) != hipSuccess) return MLAVERIFY_ERR_HIP;
+  if (ev && hipEventRecord(ev[2], s) != hipSuccess) return MLAVERIFY_ERR_HIP;
   hd->last_batch = batch;
   return MLAVERIFY_OK;
 }
@@ -279,7 +267,7 @@ int mlaverify_read_device_errors(mlaverify_t hd, void* stream, uint32_t* flags) 
 int mlaverify_profile_begin(mlaverify_t hd, int32_t max_runs) {
   if (!hd || max_runs < 1 || max_runs > (1 << 20)) return MLAVERIFY_ERR_INVALID_ARG;
   release_profile(hd);
-  hd->prof_events.resize(4 * (size_t)max_runs);
+  hd->prof_events.resize(3 * (size_t)max_runs);
   for (size_t i = 0; i < hd->prof_events.size(); i++) {
     if (hipEventCreate(&hd->prof_events[i]) != hipSuccess) {
       hd->prof_events.resize(i);
@@ -296,10 +284,10 @@ int mlaverify_profile_end(mlaverify_t hd, float* host_ms, int32_t capacity_runs)
   if (!hd || capacity_runs < 0 || (capacity_runs > 0 && !host_ms)) return MLAVERIFY_ERR_INVALID_ARG;
   const int runs = hd->prof_runs;
   int rc = runs;
-  if (runs > 0 && hipEventSynchronize(hd->prof_events[4 * runs - 1]) != hipSuccess) rc = MLAVERIFY_ERR_HIP;
+  if (runs > 0 && hipEventSynchronize(hd->prof_events[3 * runs - 1]) != hipSuccess) rc = MLAVERIFY_ERR_HIP;
   for (int i = 0; rc >= 0 && i < runs && i < capacity_runs; i++)
-    for (int k = 0; k < 3; k++)
-      if (hipEventElapsedTime(&host_ms[3 * i + k], hd->prof_events[4 * i + k], hd->prof_events[4 * i + k + 1]) !=
+    for (int k = 0; k < 2; k++)
+      if (hipEventElapsedTime(&host_ms[2 * i + k], hd->prof_events[3 * i + k], hd->prof_events[3 * i + k + 1]) !=
           hipSuccess)
         rc = MLAVERIFY_ERR_HIP;
   release_profile(hd);

@@ -1,13 +1,12 @@
 // gfx950 kernels of DDTree MLA tree-verify attention.
 //
-//   k_plan        one workgroup: validates prefix lengths and tree parents, builds the
-//                 ancestor-or-self bitmask of every tree node, and lays out the split-KV
-//                 work units (request key offsets, split length, unit table).
-//   k_partial     one workgroup per (split unit, 128-row M tile): gathers the unit's KV
-//                 rows through the page_size=1 index table into LDS, computes
-//                 S^T = K Q^T and O^T += V^T P^T on bf16 MFMA (32x32x16), with the
-//                 online softmax kept in registers; the last unit of a request also
-//                 covers the draft-tree keys under the ancestor mask.
+//   k_partial     one workgroup per (split unit, 128-row M tile).  It first derives the work
+//                 partition from the prefix lengths (every workgroup computes the same
+//                 plan; workgroup 0 also publishes it), then gathers the unit's KV rows
+//                 through the page_size=1 index table into LDS and computes
+//                 S^T = K Q^T and O^T += V^T P^T on bf16 MFMA (32x32x16), with the softmax
+//                 kept in registers; the last unit of a request also covers the draft-tree
+//                 keys under the ancestor-or-self bitmask it builds in LDS.
 //   k_merge       merges the unit partials of every row by their log-sum-exp.
 //   k_tree_masks  the bitmask step alone (one wave per request).
 //
@@ -49,100 +48,6 @@ __device__ __forceinline__ uint64_t ancestor_mask(const int32_t* __restrict__ pa
   return m;
 }
 
-// Inclusive scan over the kPlanThreads threads of the block (Hillis-Steele in LDS).
-__device__ int block_inclusive_scan(int v, int* s) {
-  const int tid = threadIdx.x;
-  s[tid] = v;
-  __syncthreads();
-  for (int off = 1; off < kPlanThreads; off <<= 1) {
-    const int t = tid >= off ? s[tid - off] : 0;
-    __syncthreads();
-    s[tid] += t;
-    __syncthreads();
-  }
-  return s[tid];
-}
-
-__global__ __launch_bounds__(kPlanThreads) void k_plan(PlanArgs a) {
-  __shared__ int s_scan[kPlanThreads];
-  __shared__ uint32_t s_err[kPlanThreads];
-  const int tid = threadIdx.x;
-  const int B = a.batch, T = a.T;
-  s_err[tid] = 0;
-  __syncthreads();
-
-  // Tree-ancestor bitmasks: one node per thread.
-  for (int n = tid; n < B * T; n += kPlanThreads) {
-    const int b = n / T, i = n - b * T;
-    bool bad = false;
-    const uint64_t m = ancestor_mask(a.tree_parent + (size_t)b * T, i, bad);
-    if (bad) atomicOr(&s_err[b], kErrBadParent);
-    a.masks[n] = m;
-  }
-  int P = 0;
-  if (tid < B) {
-    P = a.prefix_lens[tid];
-    if (P < 0 || P > a.max_prefix) {
-      atomicOr(&s_err[tid], kErrBadPrefix);
-      P = 0;
-    }
-  }
-  __syncthreads();
-  uint32_t err = tid < B ? s_err[tid] : 0u;
-  // A prefix length outside [0, max_prefix] also hides where the later requests' index
-  // segments start, so that request and every later one are poisoned (never read).
-  const int bad_here = (tid < B && (err & kErrBadPrefix)) ? 1 : 0;
-  const int bad_upto = block_inclusive_scan(bad_here, s_scan);
-  __syncthreads();
-  if (tid < B && bad_upto > 0) {
-    err |= kErrBadPrefix;
-    P = 0;
-  }
-
-  // Key offsets: exclusive scan of P_b + T.
-  const int seg = tid < B ? P + T : 0;
-  const int seg_incl = block_inclusive_scan(seg, s_scan);
-  const int total_keys = s_scan[kPlanThreads - 1];
-  __syncthreads();
-  const int total_prefix = total_keys - B * T;
-
-  // Split length: fixed, or the shortest multiple of 32 that spreads the batch's prefix
-  // tokens over target_units units (never below min_split).
-  int S = a.split_fixed;
-  if (S <= 0) {
-    const int per = (total_prefix + a.target_units - 1) / a.target_units;
-    S = max(a.min_split, (per + kTileKeys - 1) / kTileKeys * kTileKeys);
-  }
-  int units = tid < B ? max(1, (P + S - 1) / S) : 0;
-  const int u_incl = block_inclusive_scan(units, s_scan);
-  int total_units = s_scan[kPlanThreads - 1];
-  const int first = u_incl - units;
-  uint32_t rerr = err;
-  if (tid < B && first + units > a.units_cap) {  // cannot happen with the host's grid sizing
-    rerr |= kErrBadPrefix;
-    units = 0;
-  }
-  if (total_units > a.units_cap) total_units = a.units_cap;
-
-  if (tid < B) {
-    ReqPlan r;
-    r.key_off = seg_incl - seg;
-    r.prefix_len = P;
-    r.first_unit = first;
-    r.units = units;
-    r.err = rerr;
-    r.pad[0] = r.pad[1] = r.pad[2] = 0;
-    a.req[tid] = r;
-    for (int k = 0; k < units; k++) a.unit_tab[first + k] = tid;
-    if (rerr) atomicOr(&a.hdr->sticky_err, rerr);
-  }
-  if (tid == 0) {
-    a.hdr->split_len = S;
-    a.hdr->total_units = total_units;
-    a.hdr->n_mtiles = a.n_mtiles;
-  }
-}
-
 __global__ __launch_bounds__(64) void k_tree_masks(const int32_t* __restrict__ par, int T,
                                                     uint64_t* __restrict__ masks, uint32_t* __restrict__ err) {
   const int b = blockIdx.x, i = threadIdx.x;
@@ -169,6 +74,14 @@ __device__ __forceinline__ int swz(int key) {
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// 16-byte global -> LDS load (gfx950 global_load_lds_dwordx4): lane i's 16 bytes land at
+// LDS address m0 + 16 i.  Issued through asm so that the compiler does not make every
+// later LDS read wait for it; completion is awaited explicitly (vmcnt(0) + barrier)
+// before the tile is read.
+__device__ __forceinline__ void lds_dma16(const char* gaddr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gaddr), "s"(lds_base) : "m0");
+}
 
 // bf16 MFMA 32x32x16 issued through inline asm, so that the score accumulator lives in
 // VGPRs and the output accumulator in AGPRs (the compiler would put both in AGPRs and
@@ -279,15 +192,149 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float x, float y) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));  // v_cvt_pk_bf16_f32 (RNE)
 }
 
+// Partner value across the two 32-lane halves of a wave (rows live in lanes l and l + 32).
+__device__ __forceinline__ float xhalf_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Exclusive scan of one int per thread over the kThreads threads of the workgroup.
+__device__ int wg_exclusive_scan(int v, int* s_tmp, int& total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) s_tmp[w] = x;
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int k = 0; k < kWaves; k++) {
+    const int t = s_tmp[k];
+    if (k < w) base += t;
+    tot += t;
+  }
+  __syncthreads();
+  total = tot;
+  return base + x - v;
+}
+
+// Work partition (row a.2), computed by every workgroup from the prefix lengths:
+//   * prefix lengths outside [0, max_prefix] are errors; such a request and every later
+//     one are poisoned (their index segments can no longer be located) and get no keys;
+//   * key_off_b = exclusive scan of (P_b + T);
+//   * split length S: fixed, or the smallest multiple of 32 spreading the batch's prefix
+//     tokens over target_units units, at least min_split;
+//   * units_b = max(1, ceil(P_b / S)), first_unit_b = exclusive scan of units_b.
+// Fills s_unit[] for unit g (request, key offset, P, first unit, units, error bits) and
+// returns the number of units.  The publishing workgroup also writes the plan out.
+struct UnitPlan {
+  int b, key_off, prefix, first, units, split;
+  uint32_t err;
+};
+
+__device__ int plan_units(const PartialArgs& a, int g, bool publish, int* s_tmp, int* s_unit) {
+  const int tid = threadIdx.x;
+  const int B = a.batch, T = a.T;
+  constexpr int kPer = kMaxBatch / kThreads;  // requests per thread
+  int pv[kPer], bad[kPer];
+  int nbad = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; j++) {
+    const int i = kPer * tid + j;
+    pv[j] = 0;
+    bad[j] = 0;
+    if (i < B) {
+      const int P = a.prefix_lens[i];
+      bad[j] = (P < 0 || P > a.max_prefix) ? 1 : 0;
+      pv[j] = P;
+    }
+    nbad += bad[j];
+  }
+  int tot_bad;
+  int run_bad = wg_exclusive_scan(nbad, s_tmp, tot_bad);
+  int segsum = 0;
+  uint32_t err[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; j++) {
+    run_bad += bad[j];
+    err[j] = run_bad > 0 ? kErrBadPrefix : 0u;
+    if (err[j]) pv[j] = 0;
+    if (kPer * tid + j < B) segsum += pv[j] + T;
+  }
+  int total_keys;
+  int key_off = wg_exclusive_scan(segsum, s_tmp, total_keys);
+  int S = a.split_fixed;
+  if (S <= 0) {
+    const int total_prefix = total_keys - B * T;
+    const int per = (total_prefix + a.target_units - 1) / a.target_units;
+    S = max(a.min_split, (per + kTileKeys - 1) / kTileKeys * kTileKeys);
+  }
+  int units[kPer], usum = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; j++) {
+    units[j] = (kPer * tid + j < B) ? max(1, (pv[j] + S - 1) / S) : 0;
+    usum += units[j];
+  }
+  int total_units;
+  int first = wg_exclusive_scan(usum, s_tmp, total_units);
+#pragma unroll
+  for (int j = 0; j < kPer; j++) {
+    const int i = kPer * tid + j;
+    if (i < B) {
+      if (g >= first && g < first + units[j]) {
+        s_unit[0] = i;
+        s_unit[1] = key_off;
+        s_unit[2] = pv[j];
+        s_unit[3] = first;
+        s_unit[4] = units[j];
+        s_unit[5] = (int)err[j];
+      }
+      if (publish) {
+        ReqPlan rp;
+        rp.key_off = key_off;
+        rp.prefix_len = pv[j];
+        rp.first_unit = first;
+        rp.units = units[j];
+        rp.err = err[j];
+        rp.pad[0] = rp.pad[1] = rp.pad[2] = 0;
+        a.req[i] = rp;
+      }
+      key_off += pv[j] + T;
+      first += units[j];
+    }
+  }
+  if (publish && tid == 0) {
+    a.hdr->split_len = S;
+    a.hdr->total_units = total_units;
+    a.hdr->n_mtiles = a.n_mtiles;
+    if (tot_bad) atomicOr(a.sticky_err, kErrBadPrefix);
+  }
+  s_unit[6] = S;  // same value in every thread
+  __syncthreads();
+  return total_units;
+}
+
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_partial(PartialArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[2 * kTileBytes + kWaves * kQLdsBytes];
   __shared__ int s_restart[2][kWaves];
+  __shared__ int s_tmp[kWaves];
+  __shared__ int s_unit[8];
+  __shared__ uint64_t s_masks[kMaxTree];
+  __shared__ int s_badpar;
   lds_char* lds = (lds_char*)smem;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
+  const uint32_t wu = __builtin_amdgcn_readfirstlane(w);  // wave index, known uniform
   const int h = lane >> 5;     // which half of the wave (k sub-block of an MFMA operand)
   const int lrow = lane & 31;  // MFMA column: query row within the wave / key within a tile
 
@@ -297,22 +344,48 @@ void k_partial(PartialArgs a) {
   const int slot = bid >> 3;
   const int mt = slot % a.n_mtiles;
   const int g = (slot / a.n_mtiles) * 8 + (bid & 7);
-  if (g >= a.hdr->total_units) return;
-  const int b = a.unit_tab[g];
-  const ReqPlan R = a.req[b];
-  if (R.err & (kErrBadParent | kErrBadPrefix)) return;  // the merge poisons this request
-  const int S = a.hdr->split_len;
-  const int u = g - R.first_unit;
+  if (tid == 0) s_badpar = 0;
+  const int total_units = plan_units(a, g, g == 0 && mt == 0, s_tmp, s_unit);
+  if (g >= total_units || g >= a.units_cap) return;
+  const int b = s_unit[0];
+  const int key_off = s_unit[1];
+  const int prefix = s_unit[2];
+  const int first_unit = s_unit[3];
+  const int nunits = s_unit[4];
+  uint32_t req_err = (uint32_t)s_unit[5];
+  const int S = s_unit[6];
+  const int u = g - first_unit;
   const int kbeg = u * S;
-  const int npk = max(0, min(S, R.prefix_len - kbeg));  // prefix keys of this unit
+  const int npk = max(0, min(S, prefix - kbeg));  // prefix keys of this unit
   const int npt = (npk + kTileKeys - 1) / kTileKeys;
-  const bool last = (u == R.units - 1);
+  const bool last = (u == nunits - 1);
   const int ntiles = npt + (last ? (a.T + kTileKeys - 1) / kTileKeys : 0);
-  const int32_t* __restrict__ pidx = a.kv_indices + R.key_off + kbeg;
-  const int32_t* __restrict__ tidx = a.kv_indices + R.key_off + R.prefix_len;
+  const int32_t* __restrict__ pidx = a.kv_indices + key_off + kbeg;
+  const int32_t* __restrict__ tidx = a.kv_indices + key_off + prefix;
 
-  // Contiguous-run fast path: if the unit's prefix slots are one run first, first+1, ...,
-  // rows are addressed from `first` without reading the index table again.
+  // Tree-ancestor bitmasks of this request (row a.1), for the unit that covers the tree.
+  if (last) {
+    if (tid < a.T) {
+      bool bad = false;
+      s_masks[tid] = ancestor_mask(a.tree_parent + (size_t)b * a.T, tid, bad);
+      if (bad) s_badpar = 1;
+    }
+    __syncthreads();
+    if (s_badpar) {
+      req_err |= kErrBadParent;
+      if (tid == 0 && mt == 0) atomicOr(a.sticky_err, kErrBadParent);
+    }
+  }
+
+  const int r = mt * kRowsPerBlock + w * kRowsPerWave + lrow;
+  const bool rvalid = r < a.M;
+  if (req_err) {  // poisoned request: NaN partials, which the merge turns into NaN rows
+    if (rvalid && h == 0) a.part_lse[(size_t)g * a.M + r] = __uint_as_float(0x7FC00000u);
+    return;
+  }
+
+  // Contiguous-run fast path (row a.5): if the unit's prefix slots are one run first,
+  // first+1, ..., rows are addressed from `first` without reading the index table again.
   int run_base = -1;
   if (!(a.flags & 1u) && npk > 0) {
     const int first = pidx[0];
@@ -324,12 +397,9 @@ void k_partial(PartialArgs a) {
     if (ok) run_base = first;
   }
 
-  // Query rows of this wave: row r of the request is (node r / H, head r % H).
-  const int r = mt * kRowsPerBlock + w * kRowsPerWave + lrow;
-  const bool rvalid = r < a.M;
-  // B operand of the score MFMA: Q[row][16kk + 8h .. +7] (bf16 pairs).  The first kQReg
-  // k-steps stay in VGPRs for the whole unit; the rest are parked in this wave's LDS slice
-  // (lane-major, conflict-free) to leave the register allocator headroom.
+  // B operand of the score MFMA: Q[row][16kk + 8h .. +7] (bf16 pairs).  Row r of the request
+  // is (node r / H, head r % H).  The first kQReg k-steps stay in VGPRs for the whole unit;
+  // the rest are parked in this wave's LDS slice (lane-major, conflict-free).
   typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
   lds_u32x4* qlds = (lds_u32x4*)(lds + 2 * kTileBytes + w * kQLdsBytes) + lane;
   u32x4 qf[kQReg];
@@ -341,12 +411,12 @@ void k_partial(PartialArgs a) {
 #pragma unroll
     for (int kk = kQReg; kk < 36; kk++) qlds[(kk - kQReg) * 64] = qp[2 * kk];
   }
-  uint64_t anc = ~0ull;
-  if (last && rvalid) anc = a.masks[(size_t)b * a.T + r / a.H];
+  const uint64_t anc = (last && rvalid) ? s_masks[r / a.H] : ~0ull;
 
   // Gather geometry: thread tid loads 9 chunks of key kt of every tile.
   const int kt = tid >> 3;
   const int kxor = (tid & 7) ^ swz(kt);
+  int bad_index = 0;
 
   auto fetch_index = [&](int t) -> int {
     if (t < npt) {
@@ -360,15 +430,14 @@ void k_partial(PartialArgs a) {
   };
   auto issue_tile = [&](int t, int idx) {
     if ((uint32_t)idx >= (uint64_t)a.pool_slots) {  // never read outside the pool
-      atomicOr(a.sticky_err, kErrBadIndex);
-      atomicOr(&a.req_rw[b].err, kErrBadIndex);
+      if (!bad_index) atomicOr(a.sticky_err, kErrBadIndex);
+      bad_index = 1;
       idx = 0;
     }
     const char* src = reinterpret_cast<const char*>(a.pool) + (size_t)idx * a.row_stride_bytes + kxor * 16;
-    lds_char* dst = lds + (t & 1) * kTileBytes + w * 1024;
+    const uint32_t dst = (uint32_t)(uintptr_t)(lds + (t & 1) * kTileBytes) + wu * 1024;
 #pragma unroll
-    for (int j = 0; j < 9; j++)
-      __builtin_amdgcn_global_load_lds((gmem_cvoid*)(src + j * 128), (lds_void*)(dst + j * 4096), 16, 0, 0);
+    for (int j = 0; j < 9; j++) lds_dma16(src + j * 128, __builtin_amdgcn_readfirstlane(dst + j * 4096));
   };
 
   // Per-lane LDS offsets.  K operand of the score MFMA: key lrow, chunk 2kk + h.
@@ -397,6 +466,7 @@ void k_partial(PartialArgs a) {
   // later probability 2^(s - mref) is kept <= 2^16.  A tile whose maximum exceeds mref by
   // more than 16 raises mref and restarts the unit (rare: it needs a score jump of > 11
   // nats after the first tile), so the output accumulator is never rescaled.
+  const float c2 = a.scale_log2;  // > 0
   float mref = -INFINITY;
   float lrun = 0.f;
   MLV_ZERO_O();  // O^T[d = 32db + ..][row] accumulates in a[0..255]
@@ -429,32 +499,58 @@ void k_partial(PartialArgs a) {
     const int tt = t - npt;
     const int nv = tree ? min(kTileKeys, a.T - tt * kTileKeys) : min(kTileKeys, npk - t * kTileKeys);
 
-    // S^T[key][row] = sum_d K[key][d] Q[row][d]
+    // S^T[key][row] = sum_d K[key][d] Q[row][d]: 9 groups of 4 k-steps; the operands of
+    // group j+1 are read from LDS while the MFMAs of group j run.
     f32x16 sacc;
+    u32x4 kc[4], qc[4];
+    auto load_group = [&](int j, u32x4(&kr)[4], u32x4(&qr)[4]) {
 #pragma unroll
-    for (int kk = 0; kk < 36; kk++) {
-      const u32x4 kv = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
-          kb + (kk >> 2) * 4096 + koff[kk & 3]);
-      const u32x4 qv = kk < kQReg ? qf[kk < kQReg ? kk : 0] : qlds[(kk < kQReg ? 0 : kk - kQReg) * 64];
-      if (kk == 0)
-        mfma_first_v(sacc, kv, qv);
-      else
-        mfma_acc_v(sacc, kv, qv);
+      for (int c = 0; c < 4; c++) {
+        const int kk = 4 * j + c;
+        kr[c] = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(kb + j * 4096 + koff[c]);
+        qr[c] = kk < kQReg ? qf[kk < kQReg ? kk : 0] : qlds[(kk < kQReg ? 0 : kk - kQReg) * 64];
+      }
+    };
+    load_group(0, kc, qc);
+#pragma unroll
+    for (int j = 0; j < 9; j++) {
+      u32x4 kn[4], qn[4];
+      if (j + 1 < 9) load_group(j + 1, kn, qn);
+#pragma unroll
+      for (int c = 0; c < 4; c++) {
+        if (j == 0 && c == 0)
+          mfma_first_v(sacc, kc[c], qc[c]);
+        else
+          mfma_acc_v(sacc, kc[c], qc[c]);
+      }
+      if (j + 1 < 9) {
+#pragma unroll
+        for (int c = 0; c < 4; c++) {
+          kc[c] = kn[c];
+          qc[c] = qn[c];
+        }
+      }
     }
     mfma_settle_v(sacc);
 
-    // Scores of row lrow; this lane holds keys 8(v/4) + 4h + v%4 of the tile.
-    float sv[16];
+    // Row lrow's scores; this lane holds keys 8(v/4) + 4h + v%4 of the tile.  Full prefix
+    // tiles need no mask; tail and tree tiles mask with -inf.
+    const bool full = !tree && nv == kTileKeys;
     float tmax = -INFINITY;
-    const uint64_t tmask = tree ? (anc >> (tt * kTileKeys)) : ~0ull;
+    if (full) {
 #pragma unroll
-    for (int v = 0; v < 16; v++) {
-      const int key = 8 * (v >> 2) + 4 * h + (v & 3);
-      const bool vis = key < nv && ((tmask >> key) & 1ull);
-      sv[v] = vis ? sacc[v] * a.scale_log2 : -INFINITY;
-      tmax = fmaxf(tmax, sv[v]);
+      for (int v = 0; v < 16; v++) tmax = fmaxf(tmax, sacc[v]);
+    } else {
+      const uint64_t tmask = tree ? (anc >> (tt * kTileKeys)) : ~0ull;
+#pragma unroll
+      for (int v = 0; v < 16; v++) {
+        const int key = 8 * (v >> 2) + 4 * h + (v & 3);
+        const bool vis = key < nv && ((tmask >> key) & 1ull);
+        sacc[v] = vis ? sacc[v] : -INFINITY;
+        tmax = fmaxf(tmax, sacc[v]);
+      }
     }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    tmax = xhalf_max(tmax) * c2;
     const bool raise = mref != -INFINITY && tmax > mref + 16.0f;
     const bool trig = __any(raise);
     if (lane == 0) s_restart[t & 1][w] = trig ? 1 : 0;
@@ -466,11 +562,19 @@ void k_partial(PartialArgs a) {
     if (mref == -INFINITY) mref = tmax;  // first keys this row sees (may still be -inf)
 
     float p[16];
+    const float nm = -mref;
+    if (full) {
 #pragma unroll
-    for (int v = 0; v < 16; v++) {
-      p[v] = (sv[v] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sv[v] - mref);
-      lrun += p[v];
+      for (int v = 0; v < 16; v++) p[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[v], c2, nm));
+    } else {
+#pragma unroll
+      for (int v = 0; v < 16; v++)
+        p[v] = (sacc[v] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[v], c2, nm));
     }
+    float ps[8];
+#pragma unroll
+    for (int v = 0; v < 8; v++) ps[v] = p[v] + p[v + 8];
+    lrun += ((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7]));
     u32x4 pb[2];
 #pragma unroll
     for (int mf = 0; mf < 2; mf++) {
@@ -481,8 +585,7 @@ void k_partial(PartialArgs a) {
 
     // O^T[d][row] += sum_key V^T[d][key] P^T[key][row]; MFMA k index 8h + j maps to the
     // keys this lane already holds (4h + j, then 8 + 4h + j - 4; +16 for the second MFMA).
-#pragma unroll
-    for (int db = 0; db < 16; db++) {
+    auto load_v = [&](int db, u32x4(&vr)[2]) {
 #pragma unroll
       for (int mf = 0; mf < 2; mf++) {
         const lds_char* vb = kb + (db >> 1) * 4096 + mf * 16 * 128;
@@ -490,17 +593,30 @@ void k_partial(PartialArgs a) {
             (__attribute__((address_space(3))) i16x4*)(vb + voff[db & 1][0]));
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) i16x4*)(vb + 8 * 128 + voff[db & 1][1]));
-        const u32x4 vop = __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        pv_mfma(db, vop, pb[mf]);
+        vr[mf] = __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+    };
+    u32x4 vc[2];
+    load_v(0, vc);
+#pragma unroll
+    for (int db = 0; db < 16; db++) {
+      u32x4 vn[2];
+      if (db + 1 < 16) load_v(db + 1, vn);
+      pv_mfma(db, vc[0], pb[0]);
+      pv_mfma(db, vc[1], pb[1]);
+      if (db + 1 < 16) {
+        vc[0] = vn[0];
+        vc[1] = vn[1];
       }
     }
     t++;
   }
 
   asm volatile("s_nop 15\n\ts_nop 3" ::: "memory");  // last PV MFMA results settle before reads
-  const float lt = lrun + __shfl_xor(lrun, 32);
+  const int any_bad = __syncthreads_or(bad_index);
+  const float lt = xhalf_sum(lrun);
   const float inv = 1.0f / lt;
-  const float lse2 = mref + __builtin_amdgcn_logf(lt);  // log2-domain lse of this unit
+  const float lse2 = any_bad ? __uint_as_float(0x7FC00000u) : mref + __builtin_amdgcn_logf(lt);
   if (rvalid) {
     float* po = a.part_o + ((size_t)g * a.M + r) * kVdim + 4 * h;
 #pragma unroll
@@ -541,52 +657,88 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-// One thread per 4 output columns; 128 threads per row, 2 rows per workgroup.
+// One row per workgroup; wave w merges units w, w+4, ... over all 512 columns (8 per
+// lane), then the four waves combine through LDS.  A NaN partial lse (a poisoned unit)
+// makes the row NaN.
 __global__ __launch_bounds__(256) void k_merge(MergeArgs a) {
-  const int row = blockIdx.x * 2 + (threadIdx.x >> 7);
-  if (row >= a.batch * a.M) return;
-  const int c4 = threadIdx.x & 127;
+  __shared__ float s_acc[kWaves][kVdim];
+  __shared__ float s_m[kWaves], s_z[kWaves];
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int b = row / a.M, r = row - b * a.M;
-  const ReqPlan R = a.req[b];
-  uint2* po = reinterpret_cast<uint2*>(a.out + (size_t)row * kVdim) + c4;
-  if (R.err) {
-    *po = make_uint2(0x7FC07FC0u, 0x7FC07FC0u);
-    if (c4 == 0) a.lse[row] = __uint_as_float(0x7FC00000u);
-    return;
-  }
+  ReqPlan R = a.req[b];
+  R.first_unit = min(max(R.first_unit, 0), a.units_cap);  // never index past the partial buffers
+  R.units = min(R.units, a.units_cap - R.first_unit);
   const float* pl = a.part_lse + (size_t)R.first_unit * a.M + r;
+  const float* pob = a.part_o + ((size_t)R.first_unit * a.M + r) * kVdim + 8 * lane;
+  const size_t ustride = (size_t)a.M * kVdim;
   float m = -INFINITY;
-  for (int u = 0; u < R.units; u++) m = fmaxf(m, pl[(size_t)u * a.M]);
+  for (int u = w; u < R.units; u += kWaves) m = fmaxf(m, pl[(size_t)u * a.M]);
   float z = 0.f;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  const float* pob = a.part_o + ((size_t)R.first_unit * a.M + r) * kVdim + 4 * c4;
-  for (int u = 0; u < R.units; u++) {
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+  int u = w;
+  for (; u + 3 * kWaves < R.units; u += 4 * kWaves) {  // four units in flight
+    float wt[4];
+    f32x4 o0[4], o1[4];
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      const float lu = pl[(size_t)(u + k * kWaves) * a.M];
+      wt[k] = (lu == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(lu - m);
+      o0[k] = *reinterpret_cast<const f32x4*>(pob + (u + k * kWaves) * ustride);
+      o1[k] = *reinterpret_cast<const f32x4*>(pob + (u + k * kWaves) * ustride + 4);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      z += wt[k];
+      acc0 += wt[k] * o0[k];
+      acc1 += wt[k] * o1[k];
+    }
+  }
+  for (; u < R.units; u += kWaves) {
     const float lu = pl[(size_t)u * a.M];
     const float wu = (lu == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(lu - m);
-    const f32x4 o = *reinterpret_cast<const f32x4*>(pob + (size_t)u * a.M * kVdim);
     z += wu;
-    acc += wu * o;
+    acc0 += wu * *reinterpret_cast<const f32x4*>(pob + u * ustride);
+    acc1 += wu * *reinterpret_cast<const f32x4*>(pob + u * ustride + 4);
   }
-  const float inv = 1.0f / z;
-  *po = make_uint2(bf16_rne_bits(acc[0] * inv) | (bf16_rne_bits(acc[1] * inv) << 16),
-                   bf16_rne_bits(acc[2] * inv) | (bf16_rne_bits(acc[3] * inv) << 16));
-  if (c4 == 0) a.lse[row] = (m + __builtin_amdgcn_logf(z)) * 0.69314718055994531f;
+  *reinterpret_cast<f32x4*>(&s_acc[w][8 * lane]) = acc0;
+  *reinterpret_cast<f32x4*>(&s_acc[w][8 * lane + 4]) = acc1;
+  if (lane == 0) {
+    s_m[w] = m;
+    s_z[w] = z;
+  }
+  __syncthreads();
+  float M = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < kWaves; k++) M = fmaxf(M, s_m[k]);
+  float sc[kWaves], Z = 0.f;
+#pragma unroll
+  for (int k = 0; k < kWaves; k++) {
+    sc[k] = (s_m[k] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s_m[k] - M);
+    Z += sc[k] * s_z[k];
+  }
+  const float inv = 1.0f / Z;
+  const int c = 2 * tid;
+  float o[2];
+#pragma unroll
+  for (int e = 0; e < 2; e++) {
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < kWaves; k++) s += sc[k] * s_acc[k][c + e];
+    o[e] = s * inv;
+  }
+  reinterpret_cast<uint32_t*>(a.out + (size_t)row * kVdim)[tid] = bf16_rne_bits(o[0]) | (bf16_rne_bits(o[1]) << 16);
+  if (tid == 0) a.lse[row] = (M + __builtin_amdgcn_logf(Z)) * 0.69314718055994531f;
 }
 
 // ------------------------------------------------------------------------------------------
-hipError_t launch_plan(const PlanArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_plan, dim3(1), dim3(kPlanThreads), 0, s, a);
-  return hipGetLastError();
-}
-
 hipError_t launch_partial(const PartialArgs& a, int grid, hipStream_t s) {
   hipLaunchKernelGGL(k_partial, dim3(grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
-  const int rows = a.batch * a.M;
-  hipLaunchKernelGGL(k_merge, dim3((rows + 1) / 2), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_merge, dim3(a.batch * a.M), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

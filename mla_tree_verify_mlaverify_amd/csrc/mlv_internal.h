@@ -22,7 +22,6 @@ constexpr int kMaxTree = 64;
 constexpr int kMaxBatch = 1024;        // one plan thread per request
 constexpr int kTargetBlocks = 256;     // workgroups the split aims for (one per CU on MI355X)
 constexpr int kMinSplit = 128;         // shortest automatic prefix split, in tokens
-constexpr int kPlanThreads = 1024;
 
 // Device-side error bits (mirrors MLAVERIFY_DEVERR_* in the public header).
 constexpr uint32_t kErrBadParent = 0x1u;
@@ -44,37 +43,27 @@ struct ReqPlan {
   int32_t prefix_len;   // P_b after validation (0 when invalid)
   int32_t first_unit;   // global index of its first split unit
   int32_t units;        // number of split units (the last one also covers the tree)
-  uint32_t err;         // data-error bits of this request
+  uint32_t err;         // prefix-length error bits of this request
   int32_t pad[3];
 };
 static_assert(sizeof(ReqPlan) == 32, "ReqPlan size");
-
-struct PlanArgs {
-  const int32_t* prefix_lens;
-  const int32_t* tree_parent;
-  PlanHeader* hdr;
-  ReqPlan* req;
-  int32_t* unit_tab;     // unit -> request
-  uint64_t* masks;       // [batch, T] ancestor-or-self bitmasks
-  int32_t batch, T, max_prefix, split_fixed, target_units, min_split, units_cap, n_mtiles;
-};
 
 struct PartialArgs {
   const uint16_t* q;
   const uint16_t* pool;
   const int32_t* kv_indices;
-  const PlanHeader* hdr;
-  const ReqPlan* req;
-  const int32_t* unit_tab;
-  const uint64_t* masks;
+  const int32_t* prefix_lens;
+  const int32_t* tree_parent;
+  PlanHeader* hdr;       // plan published by workgroup 0 (for the merge and readback)
+  ReqPlan* req;
   float* part_o;         // [units, M, 512] unit-normalised partial outputs
-  float* part_lse;       // [units, M] log2-domain lse of each partial
+  float* part_lse;       // [units, M] log2-domain lse of each partial (NaN: poisoned)
   uint32_t* sticky_err;
-  ReqPlan* req_rw;       // for index-error reporting
   int64_t pool_slots;
   int64_t row_stride_bytes;
-  int32_t T, H, M, n_mtiles;
-  float scale_log2;      // sm_scale * log2(e)
+  int32_t batch, T, H, M, n_mtiles;
+  int32_t max_prefix, split_fixed, target_units, min_split, units_cap;
+  float scale_log2;      // sm_scale * log2(e), > 0
   uint32_t flags;
 };
 
@@ -84,11 +73,10 @@ struct MergeArgs {
   const float* part_lse;
   uint16_t* out;
   float* lse;
-  int32_t batch, M;
+  int32_t batch, M, units_cap;
 };
 
 // Launchers (kernels.hip).
-hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
 hipError_t launch_partial(const PartialArgs& a, int grid, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
 hipError_t launch_tree_masks(const int32_t* tree_parent, int batch, int T, uint64_t* masks, uint32_t* err,

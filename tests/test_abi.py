@@ -61,6 +61,8 @@ def base_cfg(**kw):
     (dict(kv_row_stride=580), binding.ERR_INVALID_ARG),
     (dict(kv_row_stride=640), binding.OK),
     (dict(sm_scale=math.inf), binding.ERR_INVALID_ARG),
+    (dict(sm_scale=0.0), binding.ERR_INVALID_ARG),
+    (dict(sm_scale=-0.07), binding.ERR_INVALID_ARG),
     (dict(split_tokens=48), binding.ERR_INVALID_ARG),
     (dict(split_tokens=-32), binding.ERR_INVALID_ARG),
     (dict(split_tokens=1024), binding.OK),
