@@ -162,7 +162,8 @@ def main() -> int:
     wall = time.perf_counter() - wall0
     kernel_ms = v.profile_end()
     call_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    assert v.read_device_errors() == 0
+    errs = v.read_device_errors()
+    assert errs == 0, errs
 
     med_ms = statistics.median(call_ms)
     p10, p90 = np.percentile(call_ms, 10), np.percentile(call_ms, 90)

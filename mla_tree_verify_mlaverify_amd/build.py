@@ -6,6 +6,7 @@ Usage: python -m mla_tree_verify_mlaverify_amd.build [--verbose]
 from __future__ import annotations
 
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -27,6 +28,9 @@ HIPCC_FLAGS = [
     "-Wall",
     # keep the compiler from forming packed fp32 VALU ops (v_pk_*_f32)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # the partial kernel keeps its output accumulator in AGPRs that only its inline asm
+    # touches; the compiler must never spill VGPRs into them (spills go to scratch instead)
+    "-mllvm", "-amdgpu-spill-vgpr-to-agpr=0",
 ]
 
 
@@ -35,6 +39,40 @@ def hipcc() -> str:
         if cand and os.path.exists(cand):
             return cand
     raise RuntimeError("hipcc not found: install ROCm or set HIPCC")
+
+
+def audit_agprs(asm: str) -> list[str]:
+    """AGPR uses outside inline asm in compiler output (each would clobber the accumulator)."""
+    bad, in_asm, func = [], False, "?"
+    agpr = re.compile(r"(?<![\w.])a(\d+|\[\d+:\d+\])")
+    for line in asm.splitlines():
+        st = line.strip()
+        if st.startswith(";;#ASMSTART"):
+            in_asm = True
+        elif st.startswith(";;#ASMEND"):
+            in_asm = False
+        elif line and not line[0].isspace() and st.endswith(":") and not st.startswith("."):
+            func = st[:-1]
+        elif not in_asm and line.startswith("\t") and st and st[0].isalpha():
+            code = st.split(";", 1)[0]
+            if agpr.search(code):
+                bad.append(f"{func}: {code}")
+    return bad
+
+
+def check_device_code(src: str, verbose: bool = False) -> None:
+    """Compile src to gfx950 assembly and refuse it if the compiler touched an AGPR."""
+    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "--cuda-device-only", "-S", src, "-o", "-"]
+    out = subprocess.run(cmd, capture_output=True, text=True)
+    if out.returncode:
+        raise RuntimeError("hipcc -S failed:\n" + out.stderr)
+    bad = audit_agprs(out.stdout)
+    if bad:
+        raise RuntimeError("compiler-generated AGPR accesses in " + src + ":\n  " + "\n  ".join(bad[:20]))
+    if verbose:
+        for m in re.finditer(r"\.name:\s+(\S+)[\s\S]*?\.private_segment_fixed_size:\s+(\d+)[\s\S]*?\.vgpr_count:\s+(\d+)",
+                             out.stdout):
+            print(f"{m.group(1)}: scratch {m.group(2)} B, vgpr+agpr {m.group(3)}", flush=True)
 
 
 def build(verbose: bool = False) -> str:
@@ -60,6 +98,7 @@ def build(verbose: bool = False) -> str:
             failed = True
     if failed:
         raise RuntimeError("hipcc failed")
+    check_device_code(os.path.join(CSRC, "kernels.hip"), verbose)
     tmp = LIB_PATH + ".tmp"
     link = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:

@@ -17,6 +17,11 @@
 
 namespace mlv {
 
+template <int N>
+struct IntC {
+  static constexpr int value = N;
+};
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -323,7 +328,7 @@ __device__ int plan_units(const PartialArgs& a, int g, bool publish, int* s_tmp,
 
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_partial(PartialArgs a) {
-  __shared__ __attribute__((aligned(1024))) char smem[2 * kTileBytes + kWaves * kQLdsBytes];
+  __shared__ __attribute__((aligned(1024))) char smem[kTileBufs * kTileBytes + kWaves * kQLdsBytes];
   __shared__ int s_restart[2][kWaves];
   __shared__ int s_tmp[kWaves];
   __shared__ int s_unit[8];
@@ -401,7 +406,7 @@ void k_partial(PartialArgs a) {
   // is (node r / H, head r % H).  The first kQReg k-steps stay in VGPRs for the whole unit;
   // the rest are parked in this wave's LDS slice (lane-major, conflict-free).
   typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
-  lds_u32x4* qlds = (lds_u32x4*)(lds + 2 * kTileBytes + w * kQLdsBytes) + lane;
+  lds_u32x4* qlds = (lds_u32x4*)(lds + kTileBufs * kTileBytes + w * kQLdsBytes) + lane;
   u32x4 qf[kQReg];
   {
     // rows past M (last M tile) read the request's last row; their results are dropped
@@ -428,16 +433,23 @@ void k_partial(PartialArgs a) {
     const int nv = min(kTileKeys, a.T - tt * kTileKeys);
     return tidx[tt * kTileKeys + (kt < nv ? kt : 0)];
   };
-  auto issue_tile = [&](int t, int idx) {
-    if ((uint32_t)idx >= (uint64_t)a.pool_slots) {  // never read outside the pool
-      if (!bad_index) atomicOr(a.sticky_err, kErrBadIndex);
-      bad_index = 1;
-      idx = 0;
-    }
-    const char* src = reinterpret_cast<const char*>(a.pool) + (size_t)idx * a.row_stride_bytes + kxor * 16;
-    const uint32_t dst = (uint32_t)(uintptr_t)(lds + (t & 1) * kTileBytes) + wu * 1024;
+  // Source row of this thread's key and the wave's LDS target.  A slot outside the pool is
+  // never read: row 0 stands in and the error is recorded when the unit ends.
+  auto tile_src = [&](int idx) -> const char* {
+    const bool oob = (uint32_t)idx >= (uint64_t)a.pool_slots;
+    bad_index |= oob ? 1 : 0;
+    const uint32_t ic = oob ? 0u : (uint32_t)idx;
+    return reinterpret_cast<const char*>(a.pool) + (uint64_t)ic * (uint64_t)a.row_stride_bytes + kxor * 16;
+  };
+  auto tile_dst = [&](int bi) -> uint32_t { return (uint32_t)(uintptr_t)(lds + bi * kTileBytes) + wu * 1024; };
+  auto issue_piece = [&](const char* src, uint32_t dst, int j) {
+    lds_dma16(src + j * 128, __builtin_amdgcn_readfirstlane(dst + j * 4096));
+  };
+  auto issue_tile = [&](int bi, int idx) {
+    const char* src = tile_src(idx);
+    const uint32_t dst = tile_dst(bi);
 #pragma unroll
-    for (int j = 0; j < 9; j++) lds_dma16(src + j * 128, __builtin_amdgcn_readfirstlane(dst + j * 4096));
+    for (int j = 0; j < 9; j++) issue_piece(src, dst, j);
   };
 
   // Per-lane LDS offsets.  K operand of the score MFMA: key lrow, chunk 2kk + h.
@@ -469,122 +481,83 @@ void k_partial(PartialArgs a) {
   const float c2 = a.scale_log2;  // > 0
   float mref = -INFINITY;
   float lrun = 0.f;
-  MLV_ZERO_O();  // O^T[d = 32db + ..][row] accumulates in a[0..255]
 
-  issue_tile(0, fetch_index(0));
-  int idx_next = ntiles > 1 ? fetch_index(1) : 0;
-  int t = 0;
-  for (;;) {
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's loads of tile t landed
-    __syncthreads();                     // ... and everyone's; tile t-1 is no longer read
-    if (t > 0) {
-      const int* fl = s_restart[(t - 1) & 1];
-      if (fl[0] | fl[1] | fl[2] | fl[3]) {  // some wave raised its reference: start over
-        t = 0;
-        MLV_ZERO_O();
-        lrun = 0.f;
-        issue_tile(0, fetch_index(0));
-        if (ntiles > 1) idx_next = fetch_index(1);
-        continue;
-      }
-    }
-    if (t == ntiles) break;
-    if (t + 1 < ntiles) {
-      issue_tile(t + 1, idx_next);
-      if (t + 2 < ntiles) idx_next = fetch_index(t + 2);
-    }
+  // S^T[key][row] = sum_d K[key][d] Q[row][d] over 36 k-steps of 16 columns.  K operand of
+  // k-step kk: key lrow, columns 16kk + 8h .. +7; its Q partner comes from VGPRs or LDS.
+  auto load_k = [&](const lds_char* kb, int kk) -> u32x4 {
+    return *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(kb + (kk >> 2) * 4096 + koff[kk & 3]);
+  };
+  auto load_q = [&](int kk) -> u32x4 {
+    return kk < kQReg ? qf[kk < kQReg ? kk : 0] : qlds[(kk < kQReg ? 0 : kk - kQReg) * 64];
+  };
 
-    const lds_char* kb = lds + (t & 1) * kTileBytes;
-    const bool tree = t >= npt;
-    const int tt = t - npt;
-    const int nv = tree ? min(kTileKeys, a.T - tt * kTileKeys) : min(kTileKeys, npk - t * kTileKeys);
-
-    // S^T[key][row] = sum_d K[key][d] Q[row][d]: 9 groups of 4 k-steps; the operands of
-    // group j+1 are read from LDS while the MFMAs of group j run.
-    f32x16 sacc;
-    u32x4 kc[4], qc[4];
-    auto load_group = [&](int j, u32x4(&kr)[4], u32x4(&qr)[4]) {
-#pragma unroll
-      for (int c = 0; c < 4; c++) {
-        const int kk = 4 * j + c;
-        kr[c] = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(kb + j * 4096 + koff[c]);
-        qr[c] = kk < kQReg ? qf[kk < kQReg ? kk : 0] : qlds[(kk < kQReg ? 0 : kk - kQReg) * 64];
-      }
-    };
-    load_group(0, kc, qc);
-#pragma unroll
-    for (int j = 0; j < 9; j++) {
-      u32x4 kn[4], qn[4];
-      if (j + 1 < 9) load_group(j + 1, kn, qn);
-#pragma unroll
-      for (int c = 0; c < 4; c++) {
-        if (j == 0 && c == 0)
-          mfma_first_v(sacc, kc[c], qc[c]);
-        else
-          mfma_acc_v(sacc, kc[c], qc[c]);
-      }
-      if (j + 1 < 9) {
-#pragma unroll
-        for (int c = 0; c < 4; c++) {
-          kc[c] = kn[c];
-          qc[c] = qn[c];
-        }
-      }
-    }
-    mfma_settle_v(sacc);
-
-    // Row lrow's scores; this lane holds keys 8(v/4) + 4h + v%4 of the tile.  Full prefix
-    // tiles need no mask; tail and tree tiles mask with -inf.
-    const bool full = !tree && nv == kTileKeys;
-    float tmax = -INFINITY;
-    if (full) {
-#pragma unroll
-      for (int v = 0; v < 16; v++) tmax = fmaxf(tmax, sacc[v]);
-    } else {
-      const uint64_t tmask = tree ? (anc >> (tt * kTileKeys)) : ~0ull;
-#pragma unroll
-      for (int v = 0; v < 16; v++) {
-        const int key = 8 * (v >> 2) + 4 * h + (v & 3);
-        const bool vis = key < nv && ((tmask >> key) & 1ull);
-        sacc[v] = vis ? sacc[v] : -INFINITY;
-        tmax = fmaxf(tmax, sacc[v]);
-      }
-    }
-    tmax = xhalf_max(tmax) * c2;
-    const bool raise = mref != -INFINITY && tmax > mref + 16.0f;
-    const bool trig = __any(raise);
-    if (lane == 0) s_restart[t & 1][w] = trig ? 1 : 0;
-    if (trig) {  // this pass is abandoned; keep the larger reference for the next one
-      mref = fmaxf(mref, tmax);
-      t++;
-      continue;
-    }
-    if (mref == -INFINITY) mref = tmax;  // first keys this row sees (may still be -inf)
-
-    float p[16];
-    const float nm = -mref;
-    if (full) {
-#pragma unroll
-      for (int v = 0; v < 16; v++) p[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[v], c2, nm));
-    } else {
-#pragma unroll
-      for (int v = 0; v < 16; v++)
-        p[v] = (sacc[v] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[v], c2, nm));
-    }
-    float ps[8];
-#pragma unroll
-    for (int v = 0; v < 8; v++) ps[v] = p[v] + p[v + 8];
-    lrun += ((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7]));
+  // Probabilities of one tile from its scores sc (this lane: keys 8(v/4) + 4h + v%4 of
+  // row lrow; invisible keys already -inf): p = 2^(s c2 - mref), packed to bf16 pairs for the
+  // PV MFMA, their sum, and the row's tile maximum (log2 units) for the reference check.
+  struct Soft {
+    float pe;  // probability of the even key of the pair being packed
+    float m;
     u32x4 pb[2];
-#pragma unroll
-    for (int mf = 0; mf < 2; mf++) {
-      const u32x4 pk = {pack_bf16x2(p[8 * mf + 0], p[8 * mf + 1]), pack_bf16x2(p[8 * mf + 2], p[8 * mf + 3]),
-                        pack_bf16x2(p[8 * mf + 4], p[8 * mf + 5]), pack_bf16x2(p[8 * mf + 6], p[8 * mf + 7])};
-      pb[mf] = pk;
+    float psum;
+    float tmax;
+  };
+  // Step i (0..35) of that computation; the steps are spread between the score MFMAs of the
+  // next tile so that the VALU work runs while the matrix core is busy.  Each probability
+  // is packed as soon as its pair is complete, so few of them are live at once.
+  auto soft_step = [&](Soft& o, const f32x16& sc, float nm, int i) {
+    if (i < 16) {
+      const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], c2, nm));
+      o.m = i == 0 ? sc[0] : fmaxf(o.m, sc[i]);
+      o.psum = i == 0 ? e : o.psum + e;
+      if (i & 1)
+        o.pb[i >> 3][(i >> 1) & 3] = pack_bf16x2(o.pe, e);
+      else
+        o.pe = e;
+    } else if (i == 16) {
+      o.tmax = xhalf_max(o.m) * c2;
     }
+  };
 
-    // O^T[d][row] += sum_key V^T[d][key] P^T[key][row]; MFMA k index 8h + j maps to the
-    // keys this lane already holds (4h + j, then 8 + 4h + j - 4; +16 for the second MFMA).
+  // One chain of 36 score MFMAs over the tile at kb.  Optionally interleaves the softmax
+  // steps of the previous tile (sc -> so) and this wave's gather pieces of a later tile:
+  // wave W issues its piece after MFMA number W of every group of four, so the four waves
+  // never queue on the CU's address unit at the same moment.  K fragments are read kSDist
+  // k-steps ahead through a ring of registers.
+  constexpr int kSDist = 3;
+  auto s_chain = [&](auto wc, auto soft, const lds_char* kb, const char* psrc, uint32_t pdst, const f32x16& sc,
+                     float nm, Soft& so) -> f32x16 {
+    constexpr int W = decltype(wc)::value;  // < 0: no gather pieces
+    constexpr bool kSoft = decltype(soft)::value != 0;
+    f32x16 acc;
+    u32x4 kr[kSDist + 1], qr[kSDist + 1];
+#pragma unroll
+    for (int i = 0; i < kSDist; i++) {
+      kr[i] = load_k(kb, i);
+      qr[i] = load_q(i);
+    }
+#pragma unroll
+    for (int i = 0; i < 36; i++) {
+      if (i + kSDist < 36) {
+        kr[(i + kSDist) % (kSDist + 1)] = load_k(kb, i + kSDist);
+        qr[(i + kSDist) % (kSDist + 1)] = load_q(i + kSDist);
+      }
+      if (i == 0)
+        mfma_first_v(acc, kr[0], qr[0]);
+      else
+        mfma_acc_v(acc, kr[i % (kSDist + 1)], qr[i % (kSDist + 1)]);
+      if (W >= 0 && (i & 3) == W) issue_piece(psrc, pdst, i >> 2);
+      if (kSoft) {
+        soft_step(so, sc, nm, i);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    mfma_settle_v(acc);
+    return acc;
+  };
+
+  // O^T[d][row] += sum_key V^T[d][key] P^T[key][row]; MFMA k index 8h + j maps to the
+  // keys this lane already holds (4h + j, then 8 + 4h + j - 4; +16 for the second MFMA).
+  auto pv_tile = [&](const lds_char* kb, const u32x4 (&pb)[2]) {
     auto load_v = [&](int db, u32x4(&vr)[2]) {
 #pragma unroll
       for (int mf = 0; mf < 2; mf++) {
@@ -609,11 +582,114 @@ void k_partial(PartialArgs a) {
         vc[1] = vn[1];
       }
     }
+  };
+
+  // Software pipeline over the tiles of the unit, three LDS buffers in rotation (tile t in
+  // buffer bi).  Iteration t: S(t+1) runs on the matrix core while the softmax of tile t
+  // runs in the gaps, and the gathers of tile t+2 are issued; then PV(t).
+  int t = 0, bi = 0;
+  bool need_init = true;  // some row of the wave has no reference yet
+  int idx_next = 0;  // this thread's key index of tile t+2
+  f32x16 sacc;       // S^T of tile t
+  Soft dummy_soft;
+  const f32x16 zero16 = {};
+  auto start_pass = [&]() {
+    t = 0;
+    bi = 0;
+    const int i0 = fetch_index(0);
+    const int i1 = ntiles > 1 ? fetch_index(1) : 0;
+    issue_tile(0, i0);
+    if (ntiles > 1) issue_tile(1, i1);
+    if (ntiles > 2) {
+      idx_next = fetch_index(2);
+      __builtin_amdgcn_s_waitcnt(0x0F7A);  // vmcnt(10): tile 0 landed (tile 1 and one index may not)
+    } else if (ntiles > 1) {
+      __builtin_amdgcn_s_waitcnt(0x0F79);  // vmcnt(9)
+    } else {
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+    }
+    __syncthreads();
+    need_init = __any(mref == -INFINITY);
+    sacc = s_chain(IntC<-1>{}, IntC<0>{}, lds, nullptr, 0u, zero16, 0.f, dummy_soft);
+  };
+  MLV_ZERO_O();  // O^T[d = 32db + ..][row] accumulates in a[0..255]
+  start_pass();
+  for (;;) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's loads of tile t+1 landed
+    __syncthreads();                     // ... and everyone's; PV(t-1) finished everywhere
+    if (t > 0) {
+      const int* fl = s_restart[(t - 1) & 1];
+      if (fl[0] | fl[1] | fl[2] | fl[3]) {  // some wave raised its reference: start over
+        asm volatile("s_nop 15\n\ts_nop 3" ::: "memory");  // PV MFMAs of the last tile have landed
+        MLV_ZERO_O();
+        lrun = 0.f;
+        start_pass();
+        continue;
+      }
+    }
+    if (t == ntiles) break;
+    const int b1 = bi == kTileBufs - 1 ? 0 : bi + 1;
+    const int b2 = b1 == kTileBufs - 1 ? 0 : b1 + 1;
+
+    // Tail and tree tiles: invisible keys get -inf (key of register v is 4h + 8(v/4) + v%4).
+    const bool tree = t >= npt;
+    const int tt = t - npt;
+    const int nv = tree ? min(kTileKeys, a.T - tt * kTileKeys) : min(kTileKeys, npk - t * kTileKeys);
+    if (tree || nv < kTileKeys) {
+      const uint32_t tm = (uint32_t)((tree ? (anc >> (tt * kTileKeys)) : ~0ull) >> (4 * h));
+      const int nvh = nv - 4 * h;
+#pragma unroll
+      for (int v = 0; v < 16; v++) {
+        const int kv = 8 * (v >> 2) + (v & 3);
+        sacc[v] = (kv < nvh && ((tm >> kv) & 1u)) ? sacc[v] : -INFINITY;
+      }
+    }
+    // A row's first visible keys set its reference (it may stay -inf if the tile hides all).
+    if (need_init) {
+      float m0 = sacc[0];
+#pragma unroll
+      for (int v = 1; v < 16; v++) m0 = fmaxf(m0, sacc[v]);
+      m0 = xhalf_max(m0) * c2;
+      if (mref == -INFINITY) mref = m0;
+      need_init = __any(mref == -INFINITY);
+    }
+    const float nm = mref == -INFINITY ? 0.f : -mref;  // all scores are -inf while mref is
+
+    // Gathers of tile t+2 go to buffer b2 (on the last tiles they re-read pool row 0 into it;
+    // nothing reads that buffer before the next barrier).
+    const char* pf_src = tile_src(t + 2 < ntiles ? idx_next : 0);
+    const uint32_t pf_dst = tile_dst(b2);
+    if (t + 3 < ntiles) idx_next = fetch_index(t + 3);
+
+    Soft so;
+    f32x16 snext;
+    if (t + 1 < ntiles) {
+      const lds_char* kb1 = lds + b1 * kTileBytes;
+      switch (wu) {
+        case 0: snext = s_chain(IntC<0>{}, IntC<1>{}, kb1, pf_src, pf_dst, sacc, nm, so); break;
+        case 1: snext = s_chain(IntC<1>{}, IntC<1>{}, kb1, pf_src, pf_dst, sacc, nm, so); break;
+        case 2: snext = s_chain(IntC<2>{}, IntC<1>{}, kb1, pf_src, pf_dst, sacc, nm, so); break;
+        default: snext = s_chain(IntC<3>{}, IntC<1>{}, kb1, pf_src, pf_dst, sacc, nm, so); break;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 36; i++) soft_step(so, sacc, nm, i);
+      snext = sacc;
+    }
+    const bool raise = mref != -INFINITY && so.tmax > mref + 16.0f;
+    const bool trig = __any(raise);
+    s_restart[t & 1][w] = trig ? 1 : 0;
+    if (raise) mref = so.tmax;  // the pass is abandoned at the next barrier; keep the larger reference
+    lrun += so.psum;
+    pv_tile(lds + bi * kTileBytes, so.pb);
+    sacc = snext;
+    bi = b1;
     t++;
   }
 
   asm volatile("s_nop 15\n\ts_nop 3" ::: "memory");  // last PV MFMA results settle before reads
   const int any_bad = __syncthreads_or(bad_index);
+  if (any_bad && tid == 0) atomicOr(a.sticky_err, kErrBadIndex);
   const float lt = xhalf_sum(lrun);
   const float inv = 1.0f / lt;
   const float lse2 = any_bad ? __uint_as_float(0x7FC00000u) : mref + __builtin_amdgcn_logf(lt);
