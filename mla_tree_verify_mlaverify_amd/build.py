@@ -31,6 +31,8 @@ HIPCC_FLAGS = [
     # the partial kernel keeps its output accumulator in AGPRs that only its inline asm
     # touches; the compiler must never spill VGPRs into them (spills go to scratch instead)
     "-mllvm", "-amdgpu-spill-vgpr-to-agpr=0",
+    # score MFMAs accumulate in VGPRs (the AGPRs are all taken by the output accumulator)
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
 
 

@@ -88,19 +88,18 @@ __device__ __forceinline__ void lds_dma16(const char* gaddr, uint32_t lds_base) 
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gaddr), "s"(lds_base) : "m0");
 }
 
-// bf16 MFMA 32x32x16 issued through inline asm, so that the score accumulator lives in
-// VGPRs and the output accumulator in AGPRs (the compiler would put both in AGPRs and
-// then shuffle the 256-register output through VGPRs every tile).  The compiler does not
-// track hazards across inline asm, so each statement carries its own wait states:
-// 3 before the MFMA (a VALU write of an operand needs 2), and mfma_settle() gives the
-// 16+ wait states an 8-pass XDL result needs before VALU or memory instructions read it.
+// Score MFMAs (bf16 32x32x16) are compiler builtins with VGPR accumulators (the library is
+// built with the VGPR form of MFMA forced), so the compiler schedules them and inserts their
+// hazard wait states.  The output accumulator is different: it sits in fixed AGPRs that only
+// inline asm touches (below), since the compiler would otherwise move the 256-register block
+// through VGPRs every tile.
 __device__ __forceinline__ void mfma_first_v(f32x16& acc, const u32x4& a, const u32x4& b) {
-  asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+  const f32x16 z = {};
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), z, 0, 0, 0);
 }
 __device__ __forceinline__ void mfma_acc_v(f32x16& acc, const u32x4& a, const u32x4& b) {
-  asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
 }
-__device__ __forceinline__ void mfma_settle_v(f32x16& acc) { asm volatile("s_nop 15\n\ts_nop 3" : "+v"(acc)); }
 
 // ---- Fixed-AGPR output accumulator: block db of O^T lives in a[16db .. 16db+15].
 // Only the asm statements below touch these registers, each declaring what it writes.
@@ -523,7 +522,7 @@ void k_partial(PartialArgs a) {
   // wave W issues its piece after MFMA number W of every group of four, so the four waves
   // never queue on the CU's address unit at the same moment.  K fragments are read kSDist
   // k-steps ahead through a ring of registers.
-  constexpr int kSDist = 3;
+  constexpr int kSDist = 2;
   auto s_chain = [&](auto wc, auto soft, const lds_char* kb, const char* psrc, uint32_t pdst, const f32x16& sc,
                      float nm, Soft& so) -> f32x16 {
     constexpr int W = decltype(wc)::value;  // < 0: no gather pieces
@@ -551,7 +550,6 @@ void k_partial(PartialArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    mfma_settle_v(acc);
     return acc;
   };
 
@@ -727,84 +725,86 @@ void k_partial(PartialArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
+  return x;
+}
+
 __device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
   const uint32_t u = __float_as_uint(x);
   if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return (u >> 16) | 0x0040u;  // quiet NaN
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-// One row per workgroup; wave w merges units w, w+4, ... over all 512 columns (8 per
-// lane), then the four waves combine through LDS.  A NaN partial lse (a poisoned unit)
-// makes the row NaN.
+// Row a.6.  kSplit workgroups per output row, each over 512/kSplit of its columns, so that
+// the grid fills the chip even when there are few rows.  The workgroup first finds
+// m = max_u lse_u (all threads loading at once), then wave w merges units w, w+4, ... with
+// kMergeDepth loads in flight (2 columns per lane) and the four waves add up through LDS.
+// A NaN partial lse (a poisoned unit) makes the row NaN.
+template <int kSplit>
 __global__ __launch_bounds__(256) void k_merge(MergeArgs a) {
-  __shared__ float s_acc[kWaves][kVdim];
+  constexpr int kCols = kVdim / kSplit;  // columns of this workgroup
+  constexpr int kPer = kCols / 64;       // columns per lane: 8, 4, 2 or 1
+  typedef float fv __attribute__((ext_vector_type(kPer)));
+  __shared__ float s_acc[kWaves][kCols];
   __shared__ float s_m[kWaves], s_z[kWaves];
-  const int row = blockIdx.x;
+  const int row = blockIdx.x / kSplit;
+  const int c0 = (blockIdx.x % kSplit) * kCols;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int b = row / a.M, r = row - b * a.M;
   ReqPlan R = a.req[b];
   R.first_unit = min(max(R.first_unit, 0), a.units_cap);  // never index past the partial buffers
   R.units = min(R.units, a.units_cap - R.first_unit);
   const float* pl = a.part_lse + (size_t)R.first_unit * a.M + r;
-  const float* pob = a.part_o + ((size_t)R.first_unit * a.M + r) * kVdim + 8 * lane;
+  const float* pob = a.part_o + ((size_t)R.first_unit * a.M + r) * kVdim + c0 + kPer * lane;
   const size_t ustride = (size_t)a.M * kVdim;
+  auto load_o = [&](int u) -> fv { return *reinterpret_cast<const fv*>(pob + u * ustride); };
+  // Reference m = max_u lse_u, with all 256 threads loading the unit lses at once.
   float m = -INFINITY;
-  for (int u = w; u < R.units; u += kWaves) m = fmaxf(m, pl[(size_t)u * a.M]);
+  for (int u = tid; u < R.units; u += kThreads) m = fmaxf(m, pl[(size_t)u * a.M]);
+  m = wave_max(m);
+  if (lane == 0) s_m[w] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
+  // wave w takes units w, w+4, ... with kMergeDepth of them in flight; lane l holds columns
+  // c0 + kPer*l .. + kPer-1
   float z = 0.f;
-  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+  fv acc = {};
   int u = w;
-  for (; u + 3 * kWaves < R.units; u += 4 * kWaves) {  // four units in flight
-    float wt[4];
-    f32x4 o0[4], o1[4];
+  for (; u + (kMergeDepth - 1) * kWaves < R.units; u += kMergeDepth * kWaves) {
+    float wt[kMergeDepth];
+    fv o[kMergeDepth];
 #pragma unroll
-    for (int k = 0; k < 4; k++) {
+    for (int k = 0; k < kMergeDepth; k++) {
       const float lu = pl[(size_t)(u + k * kWaves) * a.M];
       wt[k] = (lu == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(lu - m);
-      o0[k] = *reinterpret_cast<const f32x4*>(pob + (u + k * kWaves) * ustride);
-      o1[k] = *reinterpret_cast<const f32x4*>(pob + (u + k * kWaves) * ustride + 4);
+      o[k] = load_o(u + k * kWaves);
     }
 #pragma unroll
-    for (int k = 0; k < 4; k++) {
+    for (int k = 0; k < kMergeDepth; k++) {
       z += wt[k];
-      acc0 += wt[k] * o0[k];
-      acc1 += wt[k] * o1[k];
+      acc += wt[k] * o[k];
     }
   }
   for (; u < R.units; u += kWaves) {
     const float lu = pl[(size_t)u * a.M];
     const float wu = (lu == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(lu - m);
     z += wu;
-    acc0 += wu * *reinterpret_cast<const f32x4*>(pob + u * ustride);
-    acc1 += wu * *reinterpret_cast<const f32x4*>(pob + u * ustride + 4);
+    acc += wu * load_o(u);
   }
-  *reinterpret_cast<f32x4*>(&s_acc[w][8 * lane]) = acc0;
-  *reinterpret_cast<f32x4*>(&s_acc[w][8 * lane + 4]) = acc1;
-  if (lane == 0) {
-    s_m[w] = m;
-    s_z[w] = z;
-  }
+  *reinterpret_cast<fv*>(&s_acc[w][kPer * lane]) = acc;
+  if (lane == 0) s_z[w] = z;
   __syncthreads();
-  float M = -INFINITY;
-#pragma unroll
-  for (int k = 0; k < kWaves; k++) M = fmaxf(M, s_m[k]);
-  float sc[kWaves], Z = 0.f;
-#pragma unroll
-  for (int k = 0; k < kWaves; k++) {
-    sc[k] = (s_m[k] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s_m[k] - M);
-    Z += sc[k] * s_z[k];
-  }
+  const float Z = (s_z[0] + s_z[1]) + (s_z[2] + s_z[3]);
   const float inv = 1.0f / Z;
-  const int c = 2 * tid;
-  float o[2];
+  for (int c = 2 * tid; c < kCols; c += 2 * kThreads) {
+    float o[2];
 #pragma unroll
-  for (int e = 0; e < 2; e++) {
-    float s = 0.f;
-#pragma unroll
-    for (int k = 0; k < kWaves; k++) s += sc[k] * s_acc[k][c + e];
-    o[e] = s * inv;
+    for (int e = 0; e < 2; e++) o[e] = ((s_acc[0][c + e] + s_acc[1][c + e]) + (s_acc[2][c + e] + s_acc[3][c + e])) * inv;
+    reinterpret_cast<uint32_t*>(a.out + (size_t)row * kVdim + c0 + c)[0] = bf16_rne_bits(o[0]) | (bf16_rne_bits(o[1]) << 16);
   }
-  reinterpret_cast<uint32_t*>(a.out + (size_t)row * kVdim)[tid] = bf16_rne_bits(o[0]) | (bf16_rne_bits(o[1]) << 16);
-  if (tid == 0) a.lse[row] = (M + __builtin_amdgcn_logf(Z)) * 0.69314718055994531f;
+  if (c0 == 0 && tid == 0) a.lse[row] = (m + __builtin_amdgcn_logf(Z)) * 0.69314718055994531f;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -814,7 +814,15 @@ hipError_t launch_partial(const PartialArgs& a, int grid, hipStream_t s) {
 }
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_merge, dim3(a.batch * a.M), dim3(256), 0, s, a);
+  // about kMergeBlocks workgroups: up to 8 per row when rows are few, whole rows when many
+  const int rows = a.batch * a.M;
+  const int split = rows * 8 <= kMergeBlocks ? 8 : rows * 4 <= kMergeBlocks ? 4 : rows * 2 <= kMergeBlocks ? 2 : 1;
+  switch (split) {
+    case 8: hipLaunchKernelGGL(k_merge<8>, dim3(rows * 8), dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL(k_merge<4>, dim3(rows * 4), dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL(k_merge<2>, dim3(rows * 2), dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL(k_merge<1>, dim3(rows), dim3(256), 0, s, a); break;
+  }
   return hipGetLastError();
 }
 

@@ -17,6 +17,8 @@ constexpr int kWaves = 4;
 constexpr int kRowsPerBlock = kRowsPerWave * kWaves;  // 128 rows per workgroup (M tile)
 constexpr int kThreads = 64 * kWaves;
 constexpr int kQReg = 24;                               // Q k-steps (16 columns each) kept in VGPRs
+constexpr int kMergeDepth = 8;                        // partial loads in flight per merge wave
+constexpr int kMergeBlocks = 2048;                     // merge grid target: rows x column split
 constexpr int kTileBufs = 3;                           // KV tiles in LDS: tile t, t+1 (in use), t+2 (landing)
 constexpr int kQLdsBytes = (36 - kQReg) * 64 * 16;      // per-wave LDS slice for the other k-steps
 constexpr int kMaxTree = 64;
