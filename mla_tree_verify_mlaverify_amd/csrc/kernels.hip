@@ -444,8 +444,7 @@ void k_partial(PartialArgs a) {
   auto issue_piece = [&](const char* src, uint32_t dst, int j) {
     lds_dma16(src + j * 128, __builtin_amdgcn_readfirstlane(dst + j * 4096));
   };
-  auto issue_tile = [&](int bi, int idx) {
-    const char* src = tile_src(idx);
+  auto issue_tile = [&](int bi, const char* src) {
     const uint32_t dst = tile_dst(bi);
 #pragma unroll
     for (int j = 0; j < 9; j++) issue_piece(src, dst, j);
@@ -594,15 +593,19 @@ void k_partial(PartialArgs a) {
   auto start_pass = [&]() {
     t = 0;
     bi = 0;
+    // the three index loads go out together, before any gather (whose completion the
+    // compiler cannot see, so a wait for an index issued after one would also wait for it)
     const int i0 = fetch_index(0);
     const int i1 = ntiles > 1 ? fetch_index(1) : 0;
-    issue_tile(0, i0);
-    if (ntiles > 1) issue_tile(1, i1);
-    if (ntiles > 2) {
-      idx_next = fetch_index(2);
-      __builtin_amdgcn_s_waitcnt(0x0F7A);  // vmcnt(10): tile 0 landed (tile 1 and one index may not)
-    } else if (ntiles > 1) {
-      __builtin_amdgcn_s_waitcnt(0x0F79);  // vmcnt(9)
+    idx_next = ntiles > 2 ? fetch_index(2) : 0;
+    const char* src0 = tile_src(i0);
+    const char* src1 = tile_src(i1);
+    const int i2 = idx_next;
+    asm volatile("" ::"v"(i2));  // idx_next has landed too
+    issue_tile(0, src0);
+    if (ntiles > 1) issue_tile(1, src1);
+    if (ntiles > 1) {
+      __builtin_amdgcn_s_waitcnt(0x0F79);  // vmcnt(9): tile 0 landed (tile 1 may not)
     } else {
       __builtin_amdgcn_s_waitcnt(0x0F70);
     }
@@ -615,19 +618,25 @@ void k_partial(PartialArgs a) {
   for (;;) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's loads of tile t+1 landed
     __syncthreads();                     // ... and everyone's; PV(t-1) finished everywhere
+    int prev_flags = 0;  // some wave raised its reference at tile t-1: the pass starts over
     if (t > 0) {
       const int* fl = s_restart[(t - 1) & 1];
-      if (fl[0] | fl[1] | fl[2] | fl[3]) {  // some wave raised its reference: start over
-        asm volatile("s_nop 15\n\ts_nop 3" ::: "memory");  // PV MFMAs of the last tile have landed
-        MLV_ZERO_O();
-        lrun = 0.f;
-        start_pass();
-        continue;
-      }
+      prev_flags = fl[0] | fl[1] | fl[2] | fl[3];
     }
-    if (t == ntiles) break;
+    if (t == ntiles && !prev_flags) break;
+    // Gathers of tile t+2 go to buffer b2 (on the last tiles they re-read pool row 0 into it;
+    // nothing reads that buffer before the next barrier).
     const int b1 = bi == kTileBufs - 1 ? 0 : bi + 1;
     const int b2 = b1 == kTileBufs - 1 ? 0 : b1 + 1;
+    const char* pf_src = tile_src(t + 2 < ntiles ? idx_next : 0);
+    const uint32_t pf_dst = tile_dst(b2);
+    if (prev_flags) {
+      asm volatile("s_nop 15\n\ts_nop 3" ::: "memory");  // PV MFMAs of the last tile have landed
+      MLV_ZERO_O();
+      lrun = 0.f;
+      start_pass();
+      continue;
+    }
 
     // Tail and tree tiles: invisible keys get -inf (key of register v is 4h + 8(v/4) + v%4).
     const bool tree = t >= npt;
@@ -653,10 +662,6 @@ void k_partial(PartialArgs a) {
     }
     const float nm = mref == -INFINITY ? 0.f : -mref;  // all scores are -inf while mref is
 
-    // Gathers of tile t+2 go to buffer b2 (on the last tiles they re-read pool row 0 into it;
-    // nothing reads that buffer before the next barrier).
-    const char* pf_src = tile_src(t + 2 < ntiles ? idx_next : 0);
-    const uint32_t pf_dst = tile_dst(b2);
     if (t + 3 < ntiles) idx_next = fetch_index(t + 3);
 
     Soft so;
