@@ -61,6 +61,12 @@ SMALL = [
     (7, [513, 77, 0, 1], 17, 16, "forest", 96),
     (8, [2047], 64, 3, "random", 128),
     (9, [640, 641], 64, 2, "random", 0),
+    # limits: 128 heads (M = 8192 rows, 64 M tiles), one node of 128 heads, large batches
+    (10, [1000], 64, 128, "random", 0),
+    (11, [3000], 1, 128, "random", 0),
+    (12, [64] * 300, 2, 2, "random", 0),
+    (13, [5] * 1024, 1, 1, "chain", 0),
+    (14, [0] * 1000 + [4097], 3, 8, "random", 0),
 ]
 
 
