@@ -422,16 +422,21 @@ void k_partial(PartialArgs a) {
   const int kxor = (tid & 7) ^ swz(kt);
   int bad_index = 0;
 
-  auto fetch_index = [&](int t) -> int {
-    if (t < npt) {
-      const int nv = min(kTileKeys, npk - t * kTileKeys);
-      const int k = t * kTileKeys + (kt < nv ? kt : 0);  // tail keys re-read the tile's first key
-      return run_base >= 0 ? run_base + k : pidx[k];
-    }
-    const int tt = t - npt;
-    const int nv = min(kTileKeys, a.T - tt * kTileKeys);
-    return tidx[tt * kTileKeys + (kt < nv ? kt : 0)];
+  // Pool slot of this thread's key of tile t (tail keys re-read the tile's first key), in two
+  // steps: load_index issues the table load, slot_of turns its value into the slot once it is
+  // needed (a contiguous prefix run ignores the value), so no wait follows the load.
+  auto key_of = [&](int t) -> int {
+    const int nv = t < npt ? min(kTileKeys, npk - t * kTileKeys) : min(kTileKeys, a.T - (t - npt) * kTileKeys);
+    return kt < nv ? kt : 0;
   };
+  auto load_index = [&](int t) -> int {
+    const int32_t* ip = t < npt ? pidx + t * kTileKeys : tidx + (t - npt) * kTileKeys;
+    return ip[key_of(t)];
+  };
+  auto slot_of = [&](int t, int loaded) -> int {
+    return (t < npt && run_base >= 0) ? run_base + t * kTileKeys + key_of(t) : loaded;
+  };
+  auto fetch_index = [&](int t) -> int { return slot_of(t, load_index(t)); };
   // Source row of this thread's key and the wave's LDS target.  A slot outside the pool is
   // never read: row 0 stands in and the error is recorded when the unit ends.
   auto tile_src = [&](int idx) -> const char* {
@@ -586,7 +591,7 @@ void k_partial(PartialArgs a) {
   // runs in the gaps, and the gathers of tile t+2 are issued; then PV(t).
   int t = 0, bi = 0;
   bool need_init = true;  // some row of the wave has no reference yet
-  int idx_next = 0;  // this thread's key index of tile t+2
+  int idx_next = 0;  // this thread's loaded index-table entry of tile t+2
   f32x16 sacc;       // S^T of tile t
   Soft dummy_soft;
   const f32x16 zero16 = {};
@@ -597,7 +602,7 @@ void k_partial(PartialArgs a) {
     // compiler cannot see, so a wait for an index issued after one would also wait for it)
     const int i0 = fetch_index(0);
     const int i1 = ntiles > 1 ? fetch_index(1) : 0;
-    idx_next = ntiles > 2 ? fetch_index(2) : 0;
+    idx_next = ntiles > 2 ? load_index(2) : 0;
     const char* src0 = tile_src(i0);
     const char* src1 = tile_src(i1);
     const int i2 = idx_next;
@@ -628,7 +633,7 @@ void k_partial(PartialArgs a) {
     // nothing reads that buffer before the next barrier).
     const int b1 = bi == kTileBufs - 1 ? 0 : bi + 1;
     const int b2 = b1 == kTileBufs - 1 ? 0 : b1 + 1;
-    const char* pf_src = tile_src(t + 2 < ntiles ? idx_next : 0);
+    const char* pf_src = tile_src(t + 2 < ntiles ? slot_of(t + 2, idx_next) : 0);
     const uint32_t pf_dst = tile_dst(b2);
     if (prev_flags) {
       asm volatile("s_nop 15\n\ts_nop 3" ::: "memory");  // PV MFMAs of the last tile have landed
@@ -662,7 +667,7 @@ void k_partial(PartialArgs a) {
     }
     const float nm = mref == -INFINITY ? 0.f : -mref;  // all scores are -inf while mref is
 
-    if (t + 3 < ntiles) idx_next = fetch_index(t + 3);
+    if (t + 3 < ntiles) idx_next = load_index(t + 3);
 
     Soft so;
     f32x16 snext;
