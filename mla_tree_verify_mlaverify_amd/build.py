@@ -62,8 +62,62 @@ def audit_agprs(asm: str) -> list[str]:
     return bad
 
 
+def _vgprs(operand: str) -> set[int]:
+    m = re.fullmatch(r"v\[(\d+):(\d+)\]", operand) or re.fullmatch(r"v(\d+)", operand)
+    if not m:
+        return set()
+    lo = int(m.group(1))
+    hi = int(m.group(2)) if m.lastindex == 2 else lo
+    return set(range(lo, hi + 1))
+
+
+def audit_mfma_operands(asm: str, wait_states: int = 2) -> list[str]:
+    """Inline-asm MFMAs carry no wait states of their own, so check that no VALU instruction
+    writes one of their A/B operands within `wait_states` wait states before them (the
+    VALU-write -> MFMA-read hazard).  A label inside that window is reported too, since the
+    instruction reaching it from elsewhere is not known here."""
+    bad, in_asm, func, recent = [], False, "?", []
+    for line in asm.splitlines():
+        st = line.strip()
+        if st.startswith(";;#ASMSTART"):
+            in_asm = True
+            continue
+        if st.startswith(";;#ASMEND"):
+            in_asm = False
+            continue
+        if line and not line[0].isspace() and st.endswith(":"):
+            if st.startswith("."):
+                recent.append(("<label>", ""))  # a branch target
+            else:
+                func, recent = st[:-1], []  # a new function: nothing precedes its entry
+            continue
+        if not (line.startswith("\t") and st and st[0].isalpha()):
+            continue
+        code = st.split(";", 1)[0].strip()
+        op, _, args = code.partition(" ")
+        ops = [a.strip() for a in args.split(",")] if args else []
+        if in_asm and op.startswith("v_mfma") and len(ops) >= 3:
+            srcs = _vgprs(ops[1]) | _vgprs(ops[2])
+            ws = 0
+            for pop, pargs in reversed(recent):
+                if ws >= wait_states:
+                    break
+                if pop == "<label>":
+                    bad.append(f"{func}: label within {wait_states} wait states before {code}")
+                    break
+                if pop.startswith("v_") and not pop.startswith("v_mfma") and pargs and _vgprs(pargs[0]) & srcs:
+                    bad.append(f"{func}: {pop} {', '.join(pargs)} -> {code}")
+                    break
+                m = re.fullmatch(r"s_nop", pop)
+                ws += (int(pargs[0], 0) + 1) if m and pargs else 1
+        recent.append((op, ops))
+        recent = recent[-8:]
+    return bad
+
+
 def check_device_code(src: str, verbose: bool = False) -> None:
-    """Compile src to gfx950 assembly and refuse it if the compiler touched an AGPR."""
+    """Compile src to gfx950 assembly and refuse it if the compiler touched an AGPR or placed a
+    VALU write of an asm MFMA operand inside the hazard window."""
     cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "--cuda-device-only", "-S", src, "-o", "-"]
     out = subprocess.run(cmd, capture_output=True, text=True)
     if out.returncode:
@@ -71,6 +125,9 @@ def check_device_code(src: str, verbose: bool = False) -> None:
     bad = audit_agprs(out.stdout)
     if bad:
         raise RuntimeError("compiler-generated AGPR accesses in " + src + ":\n  " + "\n  ".join(bad[:20]))
+    bad = audit_mfma_operands(out.stdout)
+    if bad:
+        raise RuntimeError("VALU write too close before an inline-asm MFMA in " + src + ":\n  " + "\n  ".join(bad[:20]))
     if verbose:
         for m in re.finditer(r"\.name:\s+(\S+)[\s\S]*?\.private_segment_fixed_size:\s+(\d+)[\s\S]*?\.vgpr_count:\s+(\d+)",
                              out.stdout):
