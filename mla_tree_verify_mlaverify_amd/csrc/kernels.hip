@@ -537,9 +537,10 @@ void k_partial(PartialArgs a) {
   };
 
   // One chain of 36 score MFMAs over the tile at kb.  Optionally interleaves the softmax
-  // steps of the previous tile (sc -> so) and this wave's gather pieces of a later tile:
-  // wave W issues its piece after MFMA number W of every group of four, so the four waves
-  // never queue on the CU's address unit at the same moment.  K fragments are read kSDist
+  // steps of the previous tile (sc -> so) and this wave's 9 gather pieces of a later tile,
+  // one after MFMA number W of every group of four.  (Giving each wave its own W spreads the
+  // pieces over time, but four copies of the chain cost more in instruction fetch and
+  // registers than the address unit's queueing they avoid.)  K fragments are read kSDist
   // k-steps ahead through a ring of registers.
   constexpr int kSDist = 2;
   auto s_chain = [&](auto wc, auto soft, const lds_char* kb, const char* psrc, uint32_t pdst, const f32x16& sc,
@@ -688,12 +689,7 @@ void k_partial(PartialArgs a) {
     f32x16 snext;
     if (t + 1 < ntiles) {
       const lds_char* kb1 = lds + b1 * kTileBytes;
-      switch (wu) {
-        case 0: snext = s_chain(IntC<0>{}, IntC<1>{}, kb1, pf_src, pf_dst, sacc, nm, so); break;
-        case 1: snext = s_chain(IntC<1>{}, IntC<1>{}, kb1, pf_src, pf_dst, sacc, nm, so); break;
-        case 2: snext = s_chain(IntC<2>{}, IntC<1>{}, kb1, pf_src, pf_dst, sacc, nm, so); break;
-        default: snext = s_chain(IntC<3>{}, IntC<1>{}, kb1, pf_src, pf_dst, sacc, nm, so); break;
-      }
+      snext = s_chain(IntC<1>{}, IntC<1>{}, kb1, pf_src, pf_dst, sacc, nm, so);
     } else {
 #pragma unroll
       for (int i = 0; i < 36; i++) soft_step(so, sacc, nm, i);
