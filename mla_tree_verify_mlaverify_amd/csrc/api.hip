@@ -53,7 +53,7 @@ Layout layout_for(const mlaverify_config& c) {
   L.unit_tab = off;  off = align_up(off + sizeof(int32_t) * (size_t)units_cap);
   L.masks = off;     off = align_up(off + sizeof(uint64_t) * (size_t)c.max_batch * c.max_tree_nodes);
   L.part_lse = off;  off = align_up(off + sizeof(float) * (size_t)rows_cap);
-  L.part_o = off;    off = align_up(off + sizeof(float) * (size_t)rows_cap * kVdim);
+  L.part_o = off;    off = align_up(off + sizeof(uint16_t) * (size_t)rows_cap * kVdim);  // bf16
   L.total = off;
   return L;
 }
@@ -173,7 +173,7 @@ int mlaverify_run(mlaverify_t hd, int32_t batch, int32_t T, const void* q, const
   ka.tree_parent = tree_parent;
   ka.hdr = reinterpret_cast<PlanHeader*>(hd->ws + L.hdr);
   ka.req = reinterpret_cast<ReqPlan*>(hd->ws + L.req);
-  ka.part_o = reinterpret_cast<float*>(hd->ws + L.part_o);
+  ka.part_o = reinterpret_cast<uint16_t*>(hd->ws + L.part_o);
   ka.part_lse = reinterpret_cast<float*>(hd->ws + L.part_lse);
   ka.sticky_err = &ka.hdr->sticky_err;
   ka.pool_slots = c.pool_slots;

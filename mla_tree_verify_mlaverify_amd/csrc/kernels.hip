@@ -713,7 +713,10 @@ void k_partial(PartialArgs a) {
   const float inv = 1.0f / lt;
   const float lse2 = any_bad ? __uint_as_float(0x7FC00000u) : mref + __builtin_amdgcn_logf(lt);
   if (rvalid) {
-    float* po = a.part_o + ((size_t)g * a.M + r) * kVdim + 4 * h;
+    // Partials leave as bf16 (each value rounded on its own, like the probabilities fed to
+    // the PV MFMAs).  Lane pairs (lrow, h = 0/1) exchange 8-byte groups so that each lane
+    // stores 8 consecutive columns.
+    uint16_t* po = a.part_o + ((size_t)g * a.M + r) * kVdim + 8 * h;
 #pragma unroll
     for (int db = 0; db < 16; db++) {
       float X[16];
@@ -735,10 +738,15 @@ void k_partial(PartialArgs a) {
         case 14: MLV_READ_O_14(X); break;
         case 15: MLV_READ_O_15(X); break;
       }
+      uint32_t pk[8];
 #pragma unroll
-      for (int q4 = 0; q4 < 4; q4++) {
-        f32x4 v = {X[4 * q4] * inv, X[4 * q4 + 1] * inv, X[4 * q4 + 2] * inv, X[4 * q4 + 3] * inv};
-        *reinterpret_cast<f32x4*>(po + 32 * db + 8 * q4) = v;
+      for (int j = 0; j < 8; j++) pk[j] = pack_bf16x2(X[2 * j] * inv, X[2 * j + 1] * inv);
+#pragma unroll
+      for (int p = 0; p < 2; p++) {
+        const auto lo = __builtin_amdgcn_permlane32_swap(pk[4 * p], pk[4 * p + 2], false, false);
+        const auto hi = __builtin_amdgcn_permlane32_swap(pk[4 * p + 1], pk[4 * p + 3], false, false);
+        const u32x4 v = {lo[0], hi[0], lo[1], hi[1]};
+        *reinterpret_cast<u32x4*>(po + 32 * db + 16 * p) = v;
       }
     }
     if (h == 0) a.part_lse[(size_t)g * a.M + r] = lse2;
@@ -778,9 +786,10 @@ __global__ __launch_bounds__(256) void k_merge(MergeArgs a) {
   R.first_unit = min(max(R.first_unit, 0), a.units_cap);  // never index past the partial buffers
   R.units = min(R.units, a.units_cap - R.first_unit);
   const float* pl = a.part_lse + (size_t)R.first_unit * a.M + r;
-  const float* pob = a.part_o + ((size_t)R.first_unit * a.M + r) * kVdim + c0 + kPer * lane;
+  const uint16_t* pob = a.part_o + ((size_t)R.first_unit * a.M + r) * kVdim + c0 + kPer * lane;
   const size_t ustride = (size_t)a.M * kVdim;
-  auto load_o = [&](int u) -> fv { return *reinterpret_cast<const fv*>(pob + u * ustride); };
+  typedef __bf16 hv __attribute__((ext_vector_type(kPer)));  // bf16 partial values
+  auto load_o = [&](int u) -> fv { return __builtin_convertvector(*reinterpret_cast<const hv*>(pob + u * ustride), fv); };
   // Reference m = max_u lse_u, with all 256 threads loading the unit lses at once.
   float m = -INFINITY;
   for (int u = tid; u < R.units; u += kThreads) m = fmaxf(m, pl[(size_t)u * a.M]);

@@ -59,7 +59,7 @@ struct PartialArgs {
   const int32_t* tree_parent;
   PlanHeader* hdr;       // plan published by workgroup 0 (for the merge and readback)
   ReqPlan* req;
-  float* part_o;         // [units, M, 512] unit-normalised partial outputs
+  uint16_t* part_o;      // [units, M, 512] unit-normalised partial outputs (bf16 bits)
   float* part_lse;       // [units, M] log2-domain lse of each partial (NaN: poisoned)
   uint32_t* sticky_err;
   int64_t pool_slots;
@@ -72,7 +72,7 @@ struct PartialArgs {
 
 struct MergeArgs {
   const ReqPlan* req;
-  const float* part_o;
+  const uint16_t* part_o;  // bf16 bits
   const float* part_lse;
   uint16_t* out;
   float* lse;

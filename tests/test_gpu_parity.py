@@ -125,6 +125,17 @@ def test_variant_parity(variant):
         assert np.abs(ref_out).max() > 1.0  # the needle dominates somewhere
 
 
+def test_column_scales_keep_per_column_precision():
+    """V columns span 2^-12 .. 2^12 (q scaled inversely, so the scores are those of the
+    unscaled data).  Each output column divided by its scale must meet the bar of unscaled
+    data: rounding anywhere on the path must stay relative to the column itself."""
+    cfg = synth.make_config(1, variant="colscale")
+    out, lse, _ = run_gpu(cfg)
+    ref_out, ref_lse = run_oracle(cfg)
+    s = synth.column_scales()
+    print(compare(out / s, lse, ref_out / s, ref_lse))
+
+
 def test_q_zero_lse_is_log_count():
     cfg = synth.make_config(0, variant="qzero")
     out, lse, _ = run_gpu(cfg)

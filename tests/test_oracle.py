@@ -371,3 +371,18 @@ def test_sharp_queries_still_match_brute_force():
                                                   cfg["prefix_lens"], cfg["tree_parent"], SCALE)
     np.testing.assert_allclose(lse, blse, rtol=0, atol=1e-12)
     np.testing.assert_allclose(out, bout, rtol=1e-12, atol=1e-14)
+
+
+def test_column_scaling_commutes_exactly():
+    """Scaling V column d by 2^k and q column d by 2^-k leaves every score unchanged, so
+    the output column is scaled by exactly 2^k (all products and sums are exact shifts)."""
+    cfg = synth.small_config(14, batch=2, prefix=[45, 70], tree_nodes=6, heads=3, slots=512)
+    scaled = synth.apply_variant(cfg, "colscale")
+    a = orc.verify_attention(cfg["q"], cfg["pool"], cfg["kv_indices"], cfg["prefix_lens"],
+                             cfg["tree_parent"], SCALE)
+    b = orc.verify_attention(scaled["q"], scaled["pool"], scaled["kv_indices"], scaled["prefix_lens"],
+                             scaled["tree_parent"], SCALE)
+    s = synth.column_scales()
+    assert s.min() == 2.0 ** -12 and s.max() == 2.0 ** 12
+    np.testing.assert_allclose(b[0] / s, a[0], rtol=1e-12, atol=1e-16)
+    np.testing.assert_allclose(b[1], a[1], rtol=0, atol=1e-12)

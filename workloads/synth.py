@@ -264,8 +264,28 @@ def _qzero(cfg):
     return cfg
 
 
+def column_scales() -> np.ndarray:
+    """Fixed power-of-two scales, 2^-12 .. 2^12, one per V column (see ``_colscale``)."""
+    return np.exp2(((np.arange(V_DIM) * 7) % 25) - 12).astype(np.float64)
+
+
+def _colscale(cfg):
+    """Multiply V column d of every pool row by column_scales()[d] and divide q column d
+    by it.  Both are exact in bf16 (powers of two), so every score is unchanged and each
+    output column is the unscaled one times its scale; the outputs of one row then span
+    eight decades."""
+    sc = column_scales().astype(np.float32)
+    pool = cfg["pool"].copy()
+    pool[:, :V_DIM] = f32_to_bf16_bits(bf16_bits_to_f32(pool[:, :V_DIM]) * sc)
+    q = bf16_bits_to_f32(cfg["q"])
+    q[..., :V_DIM] /= sc
+    cfg["q"] = f32_to_bf16_bits(q)
+    cfg["pool"] = pool
+    return cfg
+
+
 VARIANTS = ("sorted", "contiguous", "poison_unused", "sharp", "qzero", "needle_prefix",
-            "needle_tree", "prefix0", "chain")
+            "needle_tree", "prefix0", "chain", "colscale")
 
 
 def apply_variant(cfg: dict, variant: str, rng: np.random.Generator | None = None) -> dict:
@@ -291,6 +311,8 @@ def apply_variant(cfg: dict, variant: str, rng: np.random.Generator | None = Non
         cfg = _prefix_zero(cfg)
     elif variant == "chain":
         cfg = _chain(cfg)
+    elif variant == "colscale":
+        cfg = _colscale(cfg)
     else:
         raise ValueError(f"unknown variant {variant!r}")
     cfg["variant"] = variant if cfg.get("variant") is None else cfg["variant"] + "+" + variant
