@@ -541,18 +541,31 @@ void k_partial(PartialArgs a) {
   // one after MFMA number W of every group of four.  (Giving each wave its own W spreads the
   // pieces over time, but four copies of the chain cost more in instruction fetch and
   // registers than the address unit's queueing they avoid.)  K fragments are read kSDist
-  // k-steps ahead through a ring of registers.
+  // k-steps ahead through a ring of registers; the caller reads the first kSDist of them
+  // (s_pre) as early as the tile is known to be in LDS.
   constexpr int kSDist = 2;
+  struct SPre {
+    u32x4 k[kSDist], q[kSDist];
+  };
+  auto s_pre = [&](const lds_char* kb) -> SPre {
+    SPre p;
+#pragma unroll
+    for (int i = 0; i < kSDist; i++) {
+      p.k[i] = load_k(kb, i);
+      p.q[i] = load_q(i);
+    }
+    return p;
+  };
   auto s_chain = [&](auto wc, auto soft, const lds_char* kb, const char* psrc, uint32_t pdst, const f32x16& sc,
-                     float nm, Soft& so) -> f32x16 {
+                     float nm, Soft& so, const SPre& pre) -> f32x16 {
     constexpr int W = decltype(wc)::value;  // < 0: no gather pieces
     constexpr bool kSoft = decltype(soft)::value != 0;
     f32x16 acc;
     u32x4 kr[kSDist + 1], qr[kSDist + 1];
 #pragma unroll
     for (int i = 0; i < kSDist; i++) {
-      kr[i] = load_k(kb, i);
-      qr[i] = load_q(i);
+      kr[i] = pre.k[i];
+      qr[i] = pre.q[i];
     }
 #pragma unroll
     for (int i = 0; i < 36; i++) {
@@ -575,24 +588,25 @@ void k_partial(PartialArgs a) {
 
   // O^T[d][row] += sum_key V^T[d][key] P^T[key][row]; MFMA k index 8h + j maps to the
   // keys this lane already holds (4h + j, then 8 + 4h + j - 4; +16 for the second MFMA).
-  auto pv_tile = [&](const lds_char* kb, const u32x4 (&pb)[2]) {
-    auto load_v = [&](int db, u32x4(&vr)[2]) {
+  // The caller reads the first V fragments (vc0 = load_v(kb, 0)) before its own remaining
+  // work, so that their latency is hidden.
+  auto load_v = [&](const lds_char* kb, int db, u32x4(&vr)[2]) {
 #pragma unroll
-      for (int mf = 0; mf < 2; mf++) {
-        const lds_char* vb = kb + (db >> 1) * 4096 + mf * 16 * 128;
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4*)(vb + voff[db & 1][0]));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4*)(vb + 8 * 128 + voff[db & 1][1]));
-        vr[mf] = __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      }
-    };
-    u32x4 vc[2];
-    load_v(0, vc);
+    for (int mf = 0; mf < 2; mf++) {
+      const lds_char* vb = kb + (db >> 1) * 4096 + mf * 16 * 128;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)(vb + voff[db & 1][0]));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)(vb + 8 * 128 + voff[db & 1][1]));
+      vr[mf] = __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  };
+  auto pv_tile = [&](const lds_char* kb, const u32x4 (&pb)[2], const u32x4 (&vc0)[2]) {
+    u32x4 vc[2] = {vc0[0], vc0[1]};
 #pragma unroll
     for (int db = 0; db < 16; db++) {
       u32x4 vn[2];
-      if (db + 1 < 16) load_v(db + 1, vn);
+      if (db + 1 < 16) load_v(kb, db + 1, vn);
       pv_mfma(db, vc[0], pb[0]);
       pv_mfma(db, vc[1], pb[1]);
       if (db + 1 < 16) {
@@ -632,26 +646,32 @@ void k_partial(PartialArgs a) {
     }
     __syncthreads();
     need_init = __any(mref == -INFINITY);
-    sacc = s_chain(IntC<-1>{}, IntC<0>{}, lds, nullptr, 0u, zero16, 0.f, dummy_soft);
+    sacc = s_chain(IntC<-1>{}, IntC<0>{}, lds, nullptr, 0u, zero16, 0.f, dummy_soft, s_pre(lds));
   };
   MLV_ZERO_O();  // O^T[d = 32db + ..][row] accumulates in a[0..255]
   start_pass();
   for (;;) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's loads of tile t+1 landed
     __syncthreads();                     // ... and everyone's; PV(t-1) finished everywhere
-    int prev_flags = 0;  // some wave raised its reference at tile t-1: the pass starts over
-    if (t > 0) {
-      const int* fl = s_restart[(t - 1) & 1];
-      prev_flags = fl[0] | fl[1] | fl[2] | fl[3];
-    }
-    if (t == ntiles && !prev_flags) break;
-    // Gathers of tile t+2 go to buffer b2 (on the last tiles they re-read pool row 0 into it;
-    // nothing reads that buffer before the next barrier).
+    // Reads that need only the barrier go out first (the restart flags of tile t-1 and the
+    // first fragments of S(t+1)); the index and address work below covers their latency.
+    // The rare cases (restart, end, masked tiles, first reference) are marked cold so that
+    // the steady state runs straight through.
     const int b1 = bi == kTileBufs - 1 ? 0 : bi + 1;
     const int b2 = b1 == kTileBufs - 1 ? 0 : b1 + 1;
+    const lds_char* kb1 = lds + b1 * kTileBytes;
+    const int* fl = s_restart[(t - 1) & 1];
+    const int flags = fl[0] | fl[1] | fl[2] | fl[3];
+    const SPre pre = s_pre(kb1);
+    // Gathers of tile t+2 go to buffer b2 (on the last tiles they re-read pool row 0 into it;
+    // nothing reads that buffer before the next barrier).
     const char* pf_src = tile_src(t + 2 < ntiles ? slot_of(t + 2, idx_next) : 0);
     const uint32_t pf_dst = tile_dst(b2);
-    if (prev_flags) {
+    if (t + 3 < ntiles) idx_next = load_index(t + 3);
+    const bool prev_flags = t > 0 && flags != 0;  // some wave raised its reference at tile t-1
+    if (__builtin_expect(t == ntiles || prev_flags, 0)) {
+      if (!prev_flags) break;
+      // the pass starts over with the raised references
       asm volatile("s_nop 15\n\ts_nop 3" ::: "memory");  // PV MFMAs of the last tile have landed
       MLV_ZERO_O();
       lrun = 0.f;
@@ -663,7 +683,7 @@ void k_partial(PartialArgs a) {
     const bool tree = t >= npt;
     const int tt = t - npt;
     const int nv = tree ? min(kTileKeys, a.T - tt * kTileKeys) : min(kTileKeys, npk - t * kTileKeys);
-    if (tree || nv < kTileKeys) {
+    if (__builtin_expect(tree || nv < kTileKeys, 0)) {
       const uint32_t tm = (uint32_t)((tree ? (anc >> (tt * kTileKeys)) : ~0ull) >> (4 * h));
       const int nvh = nv - 4 * h;
 #pragma unroll
@@ -673,7 +693,7 @@ void k_partial(PartialArgs a) {
       }
     }
     // A row's first visible keys set its reference (it may stay -inf if the tile hides all).
-    if (need_init) {
+    if (__builtin_expect(need_init, 0)) {
       float m0 = sacc[0];
 #pragma unroll
       for (int v = 1; v < 16; v++) m0 = fmaxf(m0, sacc[v]);
@@ -683,24 +703,24 @@ void k_partial(PartialArgs a) {
     }
     const float nm = mref == -INFINITY ? 0.f : -mref;  // all scores are -inf while mref is
 
-    if (t + 3 < ntiles) idx_next = load_index(t + 3);
-
     Soft so;
     f32x16 snext;
-    if (t + 1 < ntiles) {
-      const lds_char* kb1 = lds + b1 * kTileBytes;
-      snext = s_chain(IntC<1>{}, IntC<1>{}, kb1, pf_src, pf_dst, sacc, nm, so);
+    if (__builtin_expect(t + 1 < ntiles, 1)) {
+      snext = s_chain(IntC<1>{}, IntC<1>{}, kb1, pf_src, pf_dst, sacc, nm, so, pre);
     } else {
 #pragma unroll
       for (int i = 0; i < 36; i++) soft_step(so, sacc, nm, i);
       snext = sacc;
     }
+    const lds_char* kb = lds + bi * kTileBytes;
+    u32x4 vc0[2];
+    load_v(kb, 0, vc0);
     const bool raise = mref != -INFINITY && so.tmax > mref + 16.0f;
     const bool trig = __any(raise);
     s_restart[t & 1][w] = trig ? 1 : 0;
     if (raise) mref = so.tmax;  // the pass is abandoned at the next barrier; keep the larger reference
     lrun += so.psum;
-    pv_tile(lds + bi * kTileBytes, so.pb);
+    pv_tile(kb, so.pb, vc0);
     sacc = snext;
     bi = b1;
     t++;
