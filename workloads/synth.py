@@ -384,3 +384,31 @@ def small_config(seed: int, *, batch: int, prefix, tree_nodes: int, heads: int, 
                 slots=slots, row_stride=row_stride, sm_scale=DEFAULT_SCALE, q=q, pool=pool,
                 kv_indices=kv_indices, prefix_lens=prefix_lens, tree_parent=parents.astype(np.int32),
                 variant=None)
+
+
+def defrag_config(seed: int, *, batch: int, prefix, tree_nodes: int, heads: int, slots: int,
+                  row_stride: int = LATENT_DIM) -> dict:
+    """A relocation workload: every index of the batch is drawn (without replacement)
+    from the lower half of the pool, and ``dst_start[b]`` is the first slot of a free
+    run of P_b slots in the upper half (runs in request order, random gaps between
+    them; -1 where P_b = 0)."""
+    cfg = small_config(seed, batch=batch, prefix=prefix, tree_nodes=tree_nodes, heads=heads, slots=slots,
+                       row_stride=row_stride)
+    rng = np.random.default_rng(10_000 + seed)
+    half = slots // 2
+    total = len(cfg["kv_indices"])
+    plens = [int(p) for p in cfg["prefix_lens"]]
+    if total > half or sum(plens) > slots - half:
+        raise ValueError("pool too small for a relocation workload")
+    cfg["kv_indices"] = rng.choice(half, size=total, replace=False).astype(np.int32)
+    spare = slots - half - sum(plens)
+    gaps = np.sort(rng.integers(0, spare + 1, size=batch))
+    gaps = np.diff(np.concatenate([[0], gaps]))
+    dst, pos = [], half
+    for b, p in enumerate(plens):
+        pos += int(gaps[b])
+        dst.append(pos if p > 0 else -1)
+        pos += p
+    cfg["dst_start"] = np.asarray(dst, dtype=np.int32)
+    cfg["name"] = f"defrag_s{seed}"
+    return cfg
