@@ -6,6 +6,10 @@ workload, with its inputs resident in HBM and the caches flushed before each cal
 decode steps.  Prints one JSON line; see the design doc for the fields.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--config 3] [--warm] [--no-cpu]
+
+With --op relocate it measures Tier-1 relocation instead: one call moves a 185,000-row
+prefix, scattered over the lower half of a 524,288-slot pool, into one run in the upper
+half (the index list is restored before each call, outside the timed region).
 """
 
 from __future__ import annotations
@@ -127,6 +131,107 @@ def cpu_baseline(cfg: dict, counts: dict, budget_s: float) -> dict:
             "cpu_model": lscpu_model()}
 
 
+RELOC_SLOTS, RELOC_PREFIX, RELOC_T = 524288, 185000, 64
+RELOC_METRIC = "Tier-1 relocation GB/s (rows read + written + index list), 185k-row prefix"
+
+
+def relocation_workload(seed: int = 77) -> dict:
+    """The relocation benchmark's inputs (same recipe as its GPU parity test)."""
+    rng = np.random.default_rng(seed)
+    pool = rng.integers(0, 1 << 16, size=(RELOC_SLOTS, 576), dtype=np.uint16)  # a bytewise copy: any bits
+    idx = rng.choice(RELOC_SLOTS // 2, size=RELOC_PREFIX + RELOC_T, replace=False).astype(np.int32)
+    return dict(pool=pool, kv_indices=idx, prefix_lens=np.array([RELOC_PREFIX], dtype=np.int32),
+                dst_start=np.array([RELOC_SLOTS // 2 + 12345], dtype=np.int32))
+
+
+def relocation_bytes() -> int:
+    """Algorithmic bytes of one relocation: each row read and written once, and the prefix
+    part of the index list read and rewritten."""
+    return RELOC_PREFIX * (2 * KV_ROW_BYTES + 2 * INDEX_BYTES)
+
+
+def bench_relocate(args) -> int:
+    import torch
+
+    import mla_tree_verify_mlaverify_amd as mv
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = relocation_workload()
+    pool = torch.from_numpy(w["pool"].view(np.int16)).view(torch.bfloat16).to(dev)
+    idx0 = torch.from_numpy(w["kv_indices"]).to(dev)
+    idx = idx0.clone()
+    plens = torch.from_numpy(w["prefix_lens"]).to(dev)
+    dst = torch.from_numpy(w["dst_start"]).to(dev)
+    v = mv.Verifier(num_heads=8, max_batch=1, max_tree_nodes=RELOC_T, max_prefix_len=RELOC_PREFIX,
+                    pool_slots=RELOC_SLOTS, device=dev)
+    flush = torch.zeros(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        idx.copy_(idx0)
+        if not args.warm:
+            flush.add_(1.0)
+        v.relocate(pool, idx, plens, dst, RELOC_T, stream=stream)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    wall0 = time.perf_counter()
+    for k in range(args.steps):
+        idx.copy_(idx0)
+        if not args.warm:
+            flush.add_(1.0)
+        starts[k].record(stream)
+        v.relocate(pool, idx, plens, dst, RELOC_T, stream=stream)
+        ends[k].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    assert v.read_device_errors() == 0
+    d0 = int(w["dst_start"][0])
+    assert torch.equal(idx[:RELOC_PREFIX].cpu(), torch.arange(d0, d0 + RELOC_PREFIX, dtype=torch.int32))
+    call_ms = [s_.elapsed_time(e) for s_, e in zip(starts, ends)]
+    med_ms = statistics.median(call_ms)
+    nbytes = relocation_bytes()
+    gbs = nbytes / (med_ms * 1e-3) / 1e9
+    line = {
+        "metric": RELOC_METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(med_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u8",
+        "data": "synthetic",
+        "config": {"workload": f"relocate_p{RELOC_PREFIX}_pool{RELOC_SLOTS}", "prefix": RELOC_PREFIX,
+                   "tree_nodes": RELOC_T, "pool_slots": RELOC_SLOTS,
+                   "cache": "warm" if args.warm else "flushed 1 GiB before each call"},
+        "us_per_call": {"median": round(med_ms * 1e3, 2), "p10": round(float(np.percentile(call_ms, 10)) * 1e3, 2),
+                        "p90": round(float(np.percentile(call_ms, 90)) * 1e3, 2)},
+        "wall_s_timed_loop": round(wall, 4),
+        # the four launches of one call (prepare, mark, check, copy) timed together: the copy
+        # dominates, so the call is held to the copy's HBM roofline
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "k_reloc_* (one call)",
+                     "kernel_avg_us": round(1e3 * sum(call_ms) / len(call_ms), 2)},
+    }
+    if not args.no_cpu:
+        from oracle import relocate_oracle as rel
+
+        t0 = time.perf_counter()
+        _, _, err = rel.relocate(w["pool"], w["kv_indices"], w["prefix_lens"], RELOC_T, w["dst_start"],
+                                 RELOC_PREFIX)
+        secs = time.perf_counter() - t0
+        assert err == 0
+        line["cpu_baseline"] = {"value": round(nbytes / secs / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+                                "sample": f"one whole relocation of the same workload ({secs:.2f} s)",
+                                "cpu_model": lscpu_model()}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -138,10 +243,13 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--split", type=int, default=0, help="fixed split length (0 = automatic)")
+    ap.add_argument("--op", choices=("verify", "relocate"), default="verify")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         return 2
+    if args.op == "relocate":
+        return bench_relocate(args)
 
     import torch
 

@@ -65,6 +65,8 @@ extern "C" {
 #define MLAVERIFY_DEVERR_BAD_PREFIX 0x4u  /* a prefix_lens entry outside [0, max_prefix_len]; that
                                              request and every later one of the batch are poisoned,
                                              since their index segments can no longer be located */
+#define MLAVERIFY_DEVERR_RELOCATE_CONFLICT 0x8u /* mlaverify_relocate refused: a destination run leaves
+                                                   the pool, overlaps another one or holds a slot in use */
 
 /* Flags for mlaverify_config.flags. */
 #define MLAVERIFY_FLAG_NO_FASTPATH 0x1u   /* always gather row by row (A/B tests of the contiguous path) */
@@ -121,6 +123,35 @@ MLAVERIFY_API int mlaverify_run(mlaverify_t h, int32_t batch, int32_t tree_nodes
                                 const void* q, const void* kv_pool, const int32_t* kv_indices,
                                 const int32_t* prefix_lens, const int32_t* tree_parent,
                                 void* out, float* lse, void* stream);
+
+/* Tier-1 KV relocation (live defragmentation of prefix rows).  The "Chunk 66.0"
+ * summary calls for K/V defragmentation of the scattered page_size=1 pool; the
+ * "Chunk 66.1" summary keeps a request's KV contiguous when it is allocated (Tier 0)
+ * and defers Tier 1, moving rows that are already scattered.  This call is Tier 1:
+ * for every request b with dst_start[b] >= 0, prefix row j < P_b is copied (columns
+ * 0..575; the rest of the row stride is left alone) from pool slot
+ * kv_indices[off_b + j] to slot dst_start[b] + j, and kv_indices[off_b + j] becomes
+ * dst_start[b] + j, so that the request's prefix is one contiguous run (the case the
+ * verify pass reads without its index table).  Tree-node slots are never moved.
+ * Host arguments: batch in [1, max_batch], tree_nodes (T) in [1, max_tree_nodes],
+ * which locate the segments exactly as in mlaverify_run.  Device arguments:
+ *   kv_pool     bf16 [pool_slots, kv_row_stride] (read and written), 16-byte aligned
+ *   kv_indices  int32 [sum_b (P_b + T)], laid out as for mlaverify_run (read and written)
+ *   prefix_lens int32 [batch]
+ *   dst_start   int32 [batch]: first slot of request b's destination run, < 0 to skip b
+ * The move is all or nothing and is checked on the device before any row is copied.
+ * It is refused (pool and indices untouched, sticky bits set) when a prefix length is
+ * outside [0, max_prefix_len] (MLAVERIFY_DEVERR_BAD_PREFIX, reported alone), when an
+ * index of the batch is outside the pool (MLAVERIFY_DEVERR_BAD_INDEX), or when a
+ * destination run leaves the pool, overlaps another destination run, or contains a
+ * slot that any index of the batch uses (MLAVERIFY_DEVERR_RELOCATE_CONFLICT).  A row
+ * already at its own destination is allowed and is not copied.  Under these rules the
+ * result does not depend on the order of the copies.  The caller owns every buffer;
+ * the call uses the handle's workspace (so it is ordered with run on one stream),
+ * never synchronises, copies to the host or allocates: graph-capturable. */
+MLAVERIFY_API int mlaverify_relocate(mlaverify_t h, int32_t batch, int32_t tree_nodes, void* kv_pool,
+                                     int32_t* kv_indices, const int32_t* prefix_lens, const int32_t* dst_start,
+                                     void* stream);
 
 /* Builds the tree-ancestor bitmasks alone (the mask step of run, on its own):
  * masks[b*T + i] bit j is set iff tree node j is node i or one of its ancestors.

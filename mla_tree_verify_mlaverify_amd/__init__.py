@@ -8,6 +8,7 @@ from .binding import (  # noqa: F401
     DEVERR_BAD_INDEX,
     DEVERR_BAD_PARENT,
     DEVERR_BAD_PREFIX,
+    DEVERR_RELOCATE_CONFLICT,
     FLAG_NO_FASTPATH,
     LATENT_DIM,
     LIB_PATH,

@@ -32,6 +32,7 @@ ERR_HIP = -5
 DEVERR_BAD_PARENT = 0x1
 DEVERR_BAD_INDEX = 0x2
 DEVERR_BAD_PREFIX = 0x4
+DEVERR_RELOCATE_CONFLICT = 0x8
 
 FLAG_NO_FASTPATH = 0x1
 
@@ -41,6 +42,7 @@ EXPORTED = (
     "mlaverify_workspace_bytes",
     "mlaverify_create",
     "mlaverify_run",
+    "mlaverify_relocate",
     "mlaverify_tree_masks",
     "mlaverify_read_plan",
     "mlaverify_read_device_errors",
@@ -94,6 +96,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.mlaverify_create.restype = ctypes.c_int
     lib.mlaverify_run.argtypes = [c_void_p, c_int32, c_int32] + [c_void_p] * 8
     lib.mlaverify_run.restype = ctypes.c_int
+    lib.mlaverify_relocate.argtypes = [c_void_p, c_int32, c_int32] + [c_void_p] * 5
+    lib.mlaverify_relocate.restype = ctypes.c_int
     lib.mlaverify_tree_masks.argtypes = [c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p]
     lib.mlaverify_tree_masks.restype = ctypes.c_int
     lib.mlaverify_read_plan.argtypes = [c_void_p, c_int32, c_void_p, ctypes.POINTER(c_int32), c_int32]
@@ -221,6 +225,24 @@ class Verifier:
             raise MlaVerifyError(rc, "mlaverify_run")
         self.last_batch = b
         return out, lse
+
+    def relocate(self, kv_pool, kv_indices, prefix_lens, dst_start, tree_nodes: int, stream=None) -> None:
+        """Tier-1 relocation of the batch's prefix rows into the runs starting at dst_start
+        (in place on kv_pool and kv_indices; refusals show in read_device_errors)."""
+        dev = self.device
+        _check(prefix_lens, "prefix_lens", torch.int32, None, dev)
+        if prefix_lens.dim() != 1:
+            raise ValueError("prefix_lens must be 1-D")
+        b = prefix_lens.shape[0]
+        _check(dst_start, "dst_start", torch.int32, (b,), dev)
+        _check(kv_indices, "kv_indices", torch.int32, None, dev)
+        if kv_indices.dim() != 1:
+            raise ValueError("kv_indices must be 1-D")
+        _check(kv_pool, "kv_pool", torch.bfloat16, (self.cfg.pool_slots, self.cfg.kv_row_stride), dev)
+        rc = self.lib.mlaverify_relocate(self.handle, b, tree_nodes, kv_pool.data_ptr(), kv_indices.data_ptr(),
+                                         prefix_lens.data_ptr(), dst_start.data_ptr(), _stream_handle(stream))
+        if rc != OK:
+            raise MlaVerifyError(rc, "mlaverify_relocate")
 
     def read_plan(self, batch: int | None = None, stream=None) -> dict:
         """Work partition of the last run (synchronises the stream)."""

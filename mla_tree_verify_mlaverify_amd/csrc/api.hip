@@ -30,7 +30,7 @@ int units_for(const mlaverify_config& c, int batch, int T) {
 }
 
 struct Layout {
-  size_t hdr, req, unit_tab, masks, part_lse, part_o, total;
+  size_t hdr, req, unit_tab, masks, part_lse, part_o, reloc_off, reloc_status, reloc_maps, total;
   int units_cap;      // entries of unit_tab
   int64_t rows_cap;   // rows of part_o / part_lse
 };
@@ -54,6 +54,10 @@ Layout layout_for(const mlaverify_config& c) {
   L.masks = off;     off = align_up(off + sizeof(uint64_t) * (size_t)c.max_batch * c.max_tree_nodes);
   L.part_lse = off;  off = align_up(off + sizeof(float) * (size_t)rows_cap);
   L.part_o = off;    off = align_up(off + sizeof(uint16_t) * (size_t)rows_cap * kVdim);  // bf16
+  // relocation: segment offsets, refusal word, a bitmap and a byte map over the pool slots
+  L.reloc_off = off;    off = align_up(off + sizeof(int32_t) * (size_t)c.max_batch);
+  L.reloc_status = off; off = align_up(off + sizeof(uint32_t));
+  L.reloc_maps = off;   off = align_up(off + sizeof(uint32_t) * (size_t)(cdiv(c.pool_slots, 32) + cdiv(c.pool_slots, 4)));
   L.total = off;
   return L;
 }
@@ -210,6 +214,35 @@ int mlaverify_run(mlaverify_t hd, int32_t batch, int32_t T, const void* q, const
   if (launch_merge(ma, s) != hipSuccess) return MLAVERIFY_ERR_HIP;
   if (ev && hipEventRecord(ev[2], s) != hipSuccess) return MLAVERIFY_ERR_HIP;
   hd->last_batch = batch;
+  return MLAVERIFY_OK;
+}
+
+int mlaverify_relocate(mlaverify_t hd, int32_t batch, int32_t T, void* kv_pool, int32_t* kv_indices,
+                       const int32_t* prefix_lens, const int32_t* dst_start, void* stream) {
+  if (!hd) return MLAVERIFY_ERR_INVALID_ARG;
+  const mlaverify_config& c = hd->cfg;
+  if (batch < 1 || batch > c.max_batch || T < 1 || T > c.max_tree_nodes) return MLAVERIFY_ERR_INVALID_ARG;
+  if (!kv_pool || !kv_indices || !prefix_lens || !dst_start) return MLAVERIFY_ERR_INVALID_ARG;
+  if (!aligned(kv_pool, 16) || !aligned(kv_indices, 4) || !aligned(prefix_lens, 4) || !aligned(dst_start, 4))
+    return MLAVERIFY_ERR_INVALID_ARG;
+  const Layout& L = hd->L;
+  RelocArgs a;
+  a.pool = static_cast<char*>(kv_pool);
+  a.kv_indices = kv_indices;
+  a.prefix_lens = prefix_lens;
+  a.dst_start = dst_start;
+  a.off = reinterpret_cast<int32_t*>(hd->ws + L.reloc_off);
+  a.maps = reinterpret_cast<uint32_t*>(hd->ws + L.reloc_maps);
+  a.status = reinterpret_cast<uint32_t*>(hd->ws + L.reloc_status);
+  a.sticky_err = &reinterpret_cast<PlanHeader*>(hd->ws + L.hdr)->sticky_err;
+  a.pool_slots = c.pool_slots;
+  a.row_stride_bytes = c.kv_row_stride * 2;
+  a.map_words = cdiv(c.pool_slots, 32);
+  a.use_words = cdiv(c.pool_slots, 4);
+  a.batch = batch;
+  a.T = T;
+  a.max_prefix = c.max_prefix_len;
+  if (launch_relocate(a, static_cast<hipStream_t>(stream)) != hipSuccess) return MLAVERIFY_ERR_HIP;
   return MLAVERIFY_OK;
 }
 

@@ -30,6 +30,7 @@ constexpr int kMinSplit = 128;         // shortest automatic prefix split, in to
 constexpr uint32_t kErrBadParent = 0x1u;
 constexpr uint32_t kErrBadIndex = 0x2u;
 constexpr uint32_t kErrBadPrefix = 0x4u;
+constexpr uint32_t kErrConflict = 0x8u;   // a relocation destination is out of the pool or in use
 
 struct PlanHeader {
   int32_t split_len;     // prefix tokens per split unit
@@ -79,7 +80,26 @@ struct MergeArgs {
   int32_t batch, M, units_cap;
 };
 
-// Launchers (kernels.hip).
+// Tier-1 relocation of prefix rows (relocate.hip).
+struct RelocArgs {
+  char* pool;                  // [pool_slots, row_stride_bytes]
+  int32_t* kv_indices;         // the batch's index segments (prefix slots rewritten)
+  const int32_t* prefix_lens;  // [batch]
+  const int32_t* dst_start;    // [batch] first destination slot, < 0: request not moved
+  int32_t* off;                // [batch] segment offsets (workspace)
+  uint32_t* maps;              // [map_words + use_words] (workspace): claimed destinations (one bit
+                               // per slot), then slots in use (one byte per slot)
+  uint32_t* status;            // refusal bits of this call (workspace)
+  uint32_t* sticky_err;
+  int64_t pool_slots;
+  int64_t row_stride_bytes;
+  int64_t map_words;           // ceil(pool_slots / 32)
+  int64_t use_words;           // ceil(pool_slots / 4)
+  int batch, T, max_prefix;
+};
+
+// Launchers (kernels.hip, relocate.hip).
+hipError_t launch_relocate(const RelocArgs& a, hipStream_t s);
 hipError_t launch_partial(const PartialArgs& a, int grid, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
 hipError_t launch_tree_masks(const int32_t* tree_parent, int batch, int T, uint64_t* masks, uint32_t* err,
