@@ -48,7 +48,7 @@ def algorithmic_counts(cfg: dict) -> dict:
     kv_bytes = keys * KV_ROW_BYTES
     q_bytes = b * t * h * 576 * 2
     out_bytes = b * t * h * (512 * 2 + 4)
-    total_bytes = kv_bytes + keys * INDEX_BYTES + q_bytes + out_bytes
+    total_bytes = kv_bytes + len(cfg["kv_indices"]) * INDEX_BYTES + q_bytes + out_bytes  # one entry per page when paged
     visible = 0  # sum over (request, node) of |prefix| + |ancestors incl. self|
     for bb in range(b):
         depth = synth.tree_depths(cfg["tree_parent"][bb])
@@ -96,6 +96,9 @@ def cpu_baseline(cfg: dict, counts: dict, budget_s: float) -> dict:
     """The CPU fp64 oracle, as it stands, on the same workload (a bounded sample of its rows)."""
     from oracle import mla_tree_oracle as orc
 
+    if cfg.get("page_size", 1) > 1:  # the oracle reads one slot per token
+        cfg = dict(cfg, kv_indices=orc.expand_block_table(cfg["kv_indices"], cfg["prefix_lens"], cfg["tree_nodes"],
+                                                          cfg["page_size"]))
     try:
         from threadpoolctl import threadpool_info
 
@@ -244,6 +247,7 @@ def main() -> int:
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--split", type=int, default=0, help="fixed split length (0 = automatic)")
     ap.add_argument("--op", choices=("verify", "relocate"), default="verify")
+    ap.add_argument("--page", type=int, default=0, help="prefix page size (block table of page ids); 0 = per token")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
@@ -261,6 +265,11 @@ def main() -> int:
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     cfg = synth.make_config(args.config, variant=args.variant)
+    workload = synth.CONFIGS[args.config]["name"] + (f"+{args.variant}" if args.variant else "")
+    if args.page > 1:  # the same shapes with paged prefixes (pages drawn at random, tree slots apart)
+        cfg = synth.paged_config(args.config, batch=cfg["batch"], prefix=[int(p) for p in cfg["prefix_lens"]],
+                                 tree_nodes=cfg["tree_nodes"], heads=cfg["heads"], slots=cfg["slots"], page=args.page)
+        workload += f"+paged{args.page}"
     counts = algorithmic_counts(cfg)
 
     def bf16(a):
@@ -273,7 +282,7 @@ def main() -> int:
     kv_idx, plens, par = i32(cfg["kv_indices"]), i32(cfg["prefix_lens"]), i32(cfg["tree_parent"])
     v = mv.Verifier(num_heads=cfg["heads"], max_batch=cfg["batch"], max_tree_nodes=cfg["tree_nodes"],
                     max_prefix_len=int(cfg["prefix_lens"].max()), pool_slots=cfg["slots"],
-                    sm_scale=cfg["sm_scale"], split_tokens=args.split, device=dev)
+                    sm_scale=cfg["sm_scale"], split_tokens=args.split, page_size=args.page, device=dev)
     b, t, h = cfg["batch"], cfg["tree_nodes"], cfg["heads"]
     out = torch.empty((b * t, h, 512), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((b * t, h), dtype=torch.float32, device=dev)
@@ -324,7 +333,8 @@ def main() -> int:
         part_gbs = counts["total_bytes"] / (part_avg * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(part_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(part_gbs / HBM_PEAK_GBS, 4), "traffic": None}
-    roof["traffic"] = stored_traffic(synth.CONFIGS[args.config]["name"]) if not (args.variant or args.split or args.warm) else None
+    roof["traffic"] = (stored_traffic(synth.CONFIGS[args.config]["name"])
+                       if not (args.variant or args.split or args.warm or args.page > 1) else None)
     roof["kernel"] = "k_partial"
     roof["kernel_avg_us"] = round(part_avg * 1e3, 2)
 
@@ -341,7 +351,7 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": synth.CONFIGS[args.config]["name"] + (f"+{args.variant}" if args.variant else ""),
+        "config": {"workload": workload,
                    "batch": b, "tree_nodes": t, "heads": h,
                    "prefix_lens": [int(x) for x in cfg["prefix_lens"]], "pool_slots": cfg["slots"],
                    "split": args.split or "auto", "cache": "warm" if args.warm else "flushed 1 GiB before each call"},

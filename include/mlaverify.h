@@ -84,6 +84,10 @@ typedef struct mlaverify_config {
   int32_t split_tokens;    /* 0: choose the prefix split length per call on the device;
                               else a fixed split length in tokens, a multiple of 32 */
   uint32_t flags;          /* MLAVERIFY_FLAG_* */
+  int32_t page_size;       /* 0 or 1: one kv_indices entry (pool slot) per prefix token;
+                              else a power of two up to 1024: prefixes live in pages of
+                              page_size consecutive pool slots and their part of kv_indices
+                              is a block table of page ids (see mlaverify_run) */
 } mlaverify_config;
 
 /* Checks a configuration without touching the GPU.  Returns MLAVERIFY_OK,
@@ -108,8 +112,12 @@ MLAVERIFY_API int mlaverify_create(const mlaverify_config* cfg, void* workspace,
  * [1, max_tree_nodes].  Device arguments:
  *   q           bf16 [batch*T, H, 576], row (b*T + i)*H + h, contiguous, 16-byte aligned
  *   kv_pool     bf16 [pool_slots, kv_row_stride], 16-byte aligned; columns 0..575 are read
- *   kv_indices  int32 [sum_b (P_b + T)]: request b's P_b prefix slots in order, then the T
- *               slots holding the latents of tree nodes 0..T-1; requests back to back
+ *   kv_indices  int32 [sum_b (E_b + T)]: request b's prefix entries, then the T slots holding
+ *               the latents of tree nodes 0..T-1; requests back to back.  With page_size
+ *               <= 1, E_b = P_b and entry j is the pool slot of prefix token j.  With a page
+ *               size p > 1, E_b = ceil(P_b / p) and entry e is a page id: prefix token j lives
+ *               in pool slot entry[j / p] * p + j % p (a block table; tree slots stay per
+ *               token).  Slots outside the pool are device errors (MLAVERIFY_DEVERR_BAD_INDEX).
  *   prefix_lens int32 [batch]: P_b, 0 <= P_b <= max_prefix_len
  *   tree_parent int32 [batch, T]: -1 for a root, else a node index smaller than the node
  *   out         bf16 [batch*T, H, 512] (written), 16-byte aligned
@@ -146,7 +154,8 @@ MLAVERIFY_API int mlaverify_run(mlaverify_t h, int32_t batch, int32_t tree_nodes
  * destination run leaves the pool, overlaps another destination run, or contains a
  * slot that any index of the batch uses (MLAVERIFY_DEVERR_RELOCATE_CONFLICT).  A row
  * already at its own destination is allowed and is not copied.  Under these rules the
- * result does not depend on the order of the copies.  The caller owns every buffer;
+ * result does not depend on the order of the copies.  Needs page_size <= 1
+ * (MLAVERIFY_ERR_UNSUPPORTED otherwise).  The caller owns every buffer;
  * the call uses the handle's workspace (so it is ordered with run on one stream),
  * never synchronises, copies to the host or allocates: graph-capturable. */
 MLAVERIFY_API int mlaverify_relocate(mlaverify_t h, int32_t batch, int32_t tree_nodes, void* kv_pool,

@@ -64,6 +64,7 @@ class MlaVerifyConfig(ctypes.Structure):
         ("sm_scale", ctypes.c_float),
         ("split_tokens", ctypes.c_int32),
         ("flags", ctypes.c_uint32),
+        ("page_size", ctypes.c_int32),
     ]
 
 
@@ -126,9 +127,9 @@ def status_string(status: int) -> str:
 
 def make_config(num_heads: int, max_batch: int, max_tree_nodes: int, max_prefix_len: int,
                 pool_slots: int, kv_row_stride: int = LATENT_DIM, sm_scale: float = 1.0 / math.sqrt(192.0),
-                split_tokens: int = 0, flags: int = 0) -> MlaVerifyConfig:
+                split_tokens: int = 0, flags: int = 0, page_size: int = 0) -> MlaVerifyConfig:
     return MlaVerifyConfig(num_heads, max_batch, max_tree_nodes, max_prefix_len, pool_slots, kv_row_stride,
-                           sm_scale, split_tokens, flags)
+                           sm_scale, split_tokens, flags, page_size)
 
 
 def validate_config(cfg: MlaVerifyConfig) -> int:
@@ -169,10 +170,10 @@ class Verifier:
 
     def __init__(self, num_heads: int, max_batch: int, max_tree_nodes: int, max_prefix_len: int,
                  pool_slots: int, kv_row_stride: int = LATENT_DIM, sm_scale: float = 1.0 / math.sqrt(192.0),
-                 split_tokens: int = 0, flags: int = 0, device=None):
+                 split_tokens: int = 0, flags: int = 0, page_size: int = 0, device=None):
         self.lib = load_library()
         self.cfg = make_config(num_heads, max_batch, max_tree_nodes, max_prefix_len, pool_slots, kv_row_stride,
-                               sm_scale, split_tokens, flags)
+                               sm_scale, split_tokens, flags, page_size)
         rc = self.lib.mlaverify_validate_config(ctypes.byref(self.cfg))
         if rc != OK:
             raise MlaVerifyError(rc, "invalid configuration")

@@ -19,6 +19,12 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+int page_log2(int page_size) {
+  int lg = 0;
+  while ((1 << lg) < page_size) lg++;
+  return lg;
+}
+
 int mtiles_for(int heads, int T) { return (int)cdiv((int64_t)heads * T, kRowsPerBlock); }
 
 int target_units_for(int n_mtiles) { return (int)(cdiv(kTargetBlocks, n_mtiles) > 0 ? cdiv(kTargetBlocks, n_mtiles) : 1); }
@@ -101,6 +107,8 @@ int mlaverify_validate_config(const mlaverify_config* c) {
   if (c->split_tokens < 0 || (c->split_tokens > 0 && c->split_tokens % kTileKeys != 0))
     return MLAVERIFY_ERR_INVALID_ARG;
   if (c->flags & ~(uint32_t)MLAVERIFY_FLAG_NO_FASTPATH) return MLAVERIFY_ERR_INVALID_ARG;
+  if (c->page_size < 0 || c->page_size > kMaxPage || (c->page_size & (c->page_size - 1)) != 0)
+    return MLAVERIFY_ERR_INVALID_ARG;
   // key offsets and unit indices are 32-bit on the device
   if ((int64_t)c->max_batch * ((int64_t)c->max_prefix_len + c->max_tree_nodes) > INT32_MAX)
     return MLAVERIFY_ERR_UNSUPPORTED;
@@ -194,6 +202,8 @@ int mlaverify_run(mlaverify_t hd, int32_t batch, int32_t T, const void* q, const
   ka.units_cap = units_grid;
   ka.scale_log2 = c.sm_scale * 1.4426950408889634f;
   ka.flags = c.flags;
+  ka.page_log2 = page_log2(c.page_size);
+  ka.max_page = (int32_t)((c.pool_slots - 1) >> ka.page_log2);
 
   MergeArgs ma;
   ma.req = ka.req;
@@ -223,6 +233,7 @@ int mlaverify_relocate(mlaverify_t hd, int32_t batch, int32_t T, void* kv_pool, 
   const mlaverify_config& c = hd->cfg;
   if (batch < 1 || batch > c.max_batch || T < 1 || T > c.max_tree_nodes) return MLAVERIFY_ERR_INVALID_ARG;
   if (!kv_pool || !kv_indices || !prefix_lens || !dst_start) return MLAVERIFY_ERR_INVALID_ARG;
+  if (c.page_size > 1) return MLAVERIFY_ERR_UNSUPPORTED;  // relocation moves single-token slots
   if (!aligned(kv_pool, 16) || !aligned(kv_indices, 4) || !aligned(prefix_lens, 4) || !aligned(dst_start, 4))
     return MLAVERIFY_ERR_INVALID_ARG;
   const Layout& L = hd->L;

@@ -236,7 +236,8 @@ __device__ int wg_exclusive_scan(int v, int* s_tmp, int& total) {
 // Work partition (row a.2), computed by every workgroup from the prefix lengths:
 //   * prefix lengths outside [0, max_prefix] are errors; such a request and every later
 //     one are poisoned (their index segments can no longer be located) and get no keys;
-//   * key_off_b = exclusive scan of (P_b + T);
+//   * key_off_b = exclusive scan of (E_b + T), where E_b = ceil(P_b / page) is the number
+//     of prefix entries of the index segment (E_b = P_b when pages are single tokens);
 //   * split length S: fixed, or the smallest multiple of 32 spreading the batch's prefix
 //     tokens over target_units units, at least min_split;
 //   * units_b = max(1, ceil(P_b / S)), first_unit_b = exclusive scan of units_b.
@@ -246,6 +247,9 @@ struct UnitPlan {
   int b, key_off, prefix, first, units, split;
   uint32_t err;
 };
+
+// Entries of a prefix of p tokens in its index segment: one per page of 2^page_log2 slots.
+__device__ __forceinline__ int seg_entries(int p, int page_log2) { return (p + (1 << page_log2) - 1) >> page_log2; }
 
 __device__ int plan_units(const PartialArgs& a, int g, bool publish, int* s_tmp, int* s_unit) {
   const int tid = threadIdx.x;
@@ -267,20 +271,22 @@ __device__ int plan_units(const PartialArgs& a, int g, bool publish, int* s_tmp,
   }
   int tot_bad;
   int run_bad = wg_exclusive_scan(nbad, s_tmp, tot_bad);
-  int segsum = 0;
+  int segsum = 0, toksum = 0;
   uint32_t err[kPer];
 #pragma unroll
   for (int j = 0; j < kPer; j++) {
     run_bad += bad[j];
     err[j] = run_bad > 0 ? kErrBadPrefix : 0u;
     if (err[j]) pv[j] = 0;
-    if (kPer * tid + j < B) segsum += pv[j] + T;
+    if (kPer * tid + j < B) segsum += seg_entries(pv[j], a.page_log2) + T;
+    toksum += pv[j];
   }
   int total_keys;
   int key_off = wg_exclusive_scan(segsum, s_tmp, total_keys);
   int S = a.split_fixed;
   if (S <= 0) {
-    const int total_prefix = total_keys - B * T;
+    int total_prefix = total_keys - B * T;  // prefix tokens (entries are tokens without pages)
+    if (a.page_log2 > 0) (void)wg_exclusive_scan(toksum, s_tmp, total_prefix);
     const int per = (total_prefix + a.target_units - 1) / a.target_units;
     S = max(a.min_split, (per + kTileKeys - 1) / kTileKeys * kTileKeys);
   }
@@ -314,7 +320,7 @@ __device__ int plan_units(const PartialArgs& a, int g, bool publish, int* s_tmp,
         rp.pad[0] = rp.pad[1] = rp.pad[2] = 0;
         a.req[i] = rp;
       }
-      key_off += pv[j] + T;
+      key_off += seg_entries(pv[j], a.page_log2) + T;
       first += units[j];
     }
   }
@@ -329,6 +335,9 @@ __device__ int plan_units(const PartialArgs& a, int g, bool publish, int* s_tmp,
   return total_units;
 }
 
+// kPaged: the prefix is addressed through a block table of 2^page_log2-slot pages (the
+// index segment holds page ids); otherwise through one slot per token.
+template <bool kPaged>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_partial(PartialArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[kTileBufs * kTileBytes + kWaves * kQLdsBytes];
@@ -368,8 +377,16 @@ void k_partial(PartialArgs a) {
   const int npt = (npk + kTileKeys - 1) / kTileKeys;
   const bool last = (u == nunits - 1);
   const int ntiles = npt + (last ? (a.T + kTileKeys - 1) / kTileKeys : 0);
-  const int32_t* __restrict__ pidx = a.kv_indices + key_off + kbeg;
-  const int32_t* __restrict__ tidx = a.kv_indices + key_off + prefix;
+  // Prefix part of the index segment: per-token slots from this unit's first key on, or
+  // the request's page ids (indexed by absolute prefix position); then the tree slots.
+  const int32_t* __restrict__ pidx = a.kv_indices + key_off + (kPaged ? 0 : kbeg);
+  const int32_t* __restrict__ tidx = a.kv_indices + key_off + seg_entries(prefix, a.page_log2);
+  const int pmask = (1 << a.page_log2) - 1;
+  // Slot of prefix position pos on page id e; a page id past the pool (which could wrap
+  // when shifted) gives -1, an out-of-pool slot.
+  auto page_slot = [&](int e, int pos) -> int {
+    return (uint32_t)e <= (uint32_t)a.max_page ? (e << a.page_log2) + (pos & pmask) : -1;
+  };
 
   // Tree-ancestor bitmasks of this request (row a.1), for the unit that covers the tree.
   if (last) {
@@ -394,13 +411,16 @@ void k_partial(PartialArgs a) {
 
   // Contiguous-run fast path (row a.5): if the unit's prefix slots are one run first,
   // first+1, ..., rows are addressed from `first` without reading the index table again.
+  auto slot_at = [&](int k) -> int {  // slot of the unit's prefix key k
+    return kPaged ? page_slot(pidx[(kbeg + k) >> a.page_log2], kbeg + k) : pidx[k];
+  };
   int run_base = -1;
   if (!(a.flags & 1u) && npk > 0) {
-    const int first = pidx[0];
+    const int first = slot_at(0);
     int ok = first >= 0 && (int64_t)first + npk <= a.pool_slots;
     for (int k0 = 0; ok && k0 < npk; k0 += kThreads) {
       const int k = k0 + tid;
-      ok = __syncthreads_and(k >= npk || pidx[k] == first + k);
+      ok = __syncthreads_and(k >= npk || slot_at(k) == first + k);
     }
     if (ok) run_base = first;
   }
@@ -434,11 +454,14 @@ void k_partial(PartialArgs a) {
     return kt < nv ? kt : 0;
   };
   auto load_index = [&](int t) -> int {
+    if (kPaged && t < npt) return pidx[(kbeg + t * kTileKeys + key_of(t)) >> a.page_log2];
     const int32_t* ip = t < npt ? pidx + t * kTileKeys : tidx + (t - npt) * kTileKeys;
     return ip[key_of(t)];
   };
   auto slot_of = [&](int t, int loaded) -> int {
-    return (t < npt && run_base >= 0) ? run_base + t * kTileKeys + key_of(t) : loaded;
+    if (t < npt && run_base >= 0) return run_base + t * kTileKeys + key_of(t);
+    if (kPaged && t < npt) return page_slot(loaded, kbeg + t * kTileKeys + key_of(t));
+    return loaded;
   };
   auto fetch_index = [&](int t) -> int { return slot_of(t, load_index(t)); };
   // Source row of this thread's key and the wave's LDS target.  A slot outside the pool is
@@ -859,7 +882,10 @@ __global__ __launch_bounds__(256) void k_merge(MergeArgs a) {
 
 // ------------------------------------------------------------------------------------------
 hipError_t launch_partial(const PartialArgs& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL(k_partial, dim3(grid), dim3(kThreads), 0, s, a);
+  if (a.page_log2 > 0)
+    hipLaunchKernelGGL(k_partial<true>, dim3(grid), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_partial<false>, dim3(grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

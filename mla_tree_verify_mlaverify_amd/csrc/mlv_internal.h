@@ -22,6 +22,7 @@ constexpr int kMergeBlocks = 2048;                     // merge grid target: row
 constexpr int kTileBufs = 3;                           // KV tiles in LDS: tile t, t+1 (in use), t+2 (landing)
 constexpr int kQLdsBytes = (36 - kQReg) * 64 * 16;      // per-wave LDS slice for the other k-steps
 constexpr int kMaxTree = 64;
+constexpr int kMaxPage = 1024;         // largest prefix page (block-table) size in slots
 constexpr int kMaxBatch = 1024;        // one plan thread per request
 constexpr int kTargetBlocks = 256;     // workgroups the split aims for (one per CU on MI355X)
 constexpr int kMinSplit = 128;         // shortest automatic prefix split, in tokens
@@ -69,6 +70,8 @@ struct PartialArgs {
   int32_t max_prefix, split_fixed, target_units, min_split, units_cap;
   float scale_log2;      // sm_scale * log2(e), > 0
   uint32_t flags;
+  int32_t page_log2;     // prefix pages of 2^page_log2 slots (0: one slot per token)
+  int32_t max_page;      // largest valid page id, (pool_slots - 1) >> page_log2
 };
 
 struct MergeArgs {

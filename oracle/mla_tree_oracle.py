@@ -100,6 +100,26 @@ def request_offsets(prefix_lens, tree_nodes: int) -> np.ndarray:
     return offs
 
 
+def expand_block_table(kv_indices, prefix_lens, tree_nodes: int, page_size: int) -> np.ndarray:
+    """Per-token index list of a batch whose prefixes are paged.
+
+    A paged layout is this library's reading of a block table for the same pool (the
+    "Chunk 66.0" and "Chunk 66.1" summaries only speak of page_size=1): request b's
+    segment holds ceil(P_b / p) page ids, then its T tree slots, and prefix token j lives
+    in pool slot page_id[j // p] * p + j % p.  With p = 1 the list is unchanged.
+    """
+    idx = np.asarray(kv_indices, dtype=np.int64)
+    out, pos = [], 0
+    for p_b in np.asarray(prefix_lens).tolist():
+        n_pages = -(-int(p_b) // page_size)
+        table = idx[pos:pos + n_pages]
+        j = np.arange(int(p_b), dtype=np.int64)
+        out.append(table[j // page_size] * page_size + j % page_size)
+        out.append(idx[pos + n_pages:pos + n_pages + tree_nodes])
+        pos += n_pages + tree_nodes
+    return np.concatenate(out).astype(np.int64) if out else np.zeros(0, dtype=np.int64)
+
+
 def visible_slots(kv_indices, prefix_lens, tree_parent, b: int, i: int) -> np.ndarray:
     """Pool rows node i of request b attends to, as a list: the prefix slots, then anc*(i)'s slots."""
     tree_parent = np.asarray(tree_parent)

@@ -68,6 +68,12 @@ def base_cfg(**kw):
     (dict(split_tokens=1024), binding.OK),
     (dict(flags=0x80), binding.ERR_INVALID_ARG),
     (dict(flags=binding.FLAG_NO_FASTPATH), binding.OK),
+    (dict(page_size=1), binding.OK),
+    (dict(page_size=64), binding.OK),
+    (dict(page_size=1024), binding.OK),
+    (dict(page_size=3), binding.ERR_INVALID_ARG),     # not a power of two
+    (dict(page_size=2048), binding.ERR_INVALID_ARG),  # larger than 1024
+    (dict(page_size=-4), binding.ERR_INVALID_ARG),
     (dict(max_batch=1024, max_prefix_len=1 << 22), binding.ERR_UNSUPPORTED),  # 32-bit key offsets
 ])
 def test_validate_config(lib, kw, expect):

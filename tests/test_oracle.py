@@ -386,3 +386,27 @@ def test_column_scaling_commutes_exactly():
     assert s.min() == 2.0 ** -12 and s.max() == 2.0 ** 12
     np.testing.assert_allclose(b[0] / s, a[0], rtol=1e-12, atol=1e-16)
     np.testing.assert_allclose(b[1], a[1], rtol=0, atol=1e-12)
+
+
+def test_block_table_expansion_hand_derived():
+    # page 4: request 0 (P=6) on pages 2, 0 -> slots 8..11, 0, 1; tree slot 30.
+    # request 1 (P=3) on page 5 -> 20, 21, 22; tree slot 31.
+    idx = np.array([2, 0, 30, 5, 31])
+    got = orc.expand_block_table(idx, [6, 3], 1, 4)
+    assert got.tolist() == [8, 9, 10, 11, 0, 1, 30, 20, 21, 22, 31]
+    # page 1 leaves the list unchanged; P = 0 has no pages
+    assert orc.expand_block_table(np.array([7, 3, 9, 1, 4]), [3, 0], 1, 1).tolist() == [7, 3, 9, 1, 4]
+    assert orc.expand_block_table(np.array([9, 12]), [0, 0], 1, 64).tolist() == [9, 12]
+
+
+def test_paged_layout_attention_equals_its_expansion():
+    """The paged workload and its per-token expansion are the same attention (brute force on
+    the expanded list)."""
+    cfg = synth.paged_config(15, batch=2, prefix=[37, 70], tree_nodes=5, heads=2, slots=1024, page=16)
+    flat = orc.expand_block_table(cfg["kv_indices"], cfg["prefix_lens"], 5, 16)
+    assert len(flat) == 37 + 70 + 10 and len(set(flat.tolist())) == len(flat)
+    out, lse = orc.verify_attention(cfg["q"], cfg["pool"], flat, cfg["prefix_lens"], cfg["tree_parent"], SCALE)
+    bout, blse = orc.brute_force_verify_attention(cfg["q"], cfg["pool"], flat, cfg["prefix_lens"],
+                                                  cfg["tree_parent"], SCALE)
+    np.testing.assert_allclose(out, bout, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(lse, blse, rtol=0, atol=1e-12)

@@ -412,3 +412,33 @@ def defrag_config(seed: int, *, batch: int, prefix, tree_nodes: int, heads: int,
     cfg["dst_start"] = np.asarray(dst, dtype=np.int32)
     cfg["name"] = f"defrag_s{seed}"
     return cfg
+
+
+def paged_config(seed: int, *, batch: int, prefix, tree_nodes: int, heads: int, slots: int, page: int,
+                 contiguous_pages: bool = False) -> dict:
+    """A workload whose prefixes are paged: ``kv_indices`` holds, per request, the page ids of
+    its ceil(P_b / page) prefix pages (distinct, drawn from the pages below the top quarter of
+    the pool; consecutive from a random start when ``contiguous_pages``), then its T tree
+    slots, drawn from the top quarter.  ``page_size`` is recorded in the config."""
+    cfg = small_config(seed, batch=batch, prefix=prefix, tree_nodes=tree_nodes, heads=heads, slots=slots)
+    rng = np.random.default_rng(20_000 + seed)
+    top = slots - slots // 4
+    n_pages = [-(-int(p) // page) for p in cfg["prefix_lens"]]
+    avail = top // page
+    if sum(n_pages) > avail or batch * tree_nodes > slots - top:
+        raise ValueError("pool too small for a paged workload")
+    if contiguous_pages:
+        start = int(rng.integers(0, avail - sum(n_pages) + 1))
+        pages = np.arange(start, start + sum(n_pages))
+    else:
+        pages = rng.choice(avail, size=sum(n_pages), replace=False)
+    tree_slots = top + rng.choice(slots - top, size=batch * tree_nodes, replace=False)
+    segs, pp = [], 0
+    for b, n in enumerate(n_pages):
+        segs.append(pages[pp:pp + n])
+        segs.append(tree_slots[b * tree_nodes:(b + 1) * tree_nodes])
+        pp += n
+    cfg["kv_indices"] = np.concatenate(segs).astype(np.int32)
+    cfg["page_size"] = page
+    cfg["name"] = f"paged{page}_s{seed}"
+    return cfg
