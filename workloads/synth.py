@@ -442,3 +442,44 @@ def paged_config(seed: int, *, batch: int, prefix, tree_nodes: int, heads: int, 
     cfg["page_size"] = page
     cfg["name"] = f"paged{page}_s{seed}"
     return cfg
+
+
+def accept_config(seed: int, *, batch: int, tree_nodes: int, vocab: int, plant: bool = True) -> dict:
+    """Inputs of the acceptance step: a random tree per request (as ``random_tree``), draft
+    tokens that differ between siblings, and fp32 logits N(0, 1) of shape [B, T + 1, V].
+    With ``plant``, a random path from the first level down is made to match: the logits
+    of the row before each of its nodes get +20 at that node's token.  (Where the path
+    stops, the next argmax is random and may extend it by chance.)"""
+    rng = np.random.default_rng(30_000 + seed)
+    t = tree_nodes
+    parents = np.stack([random_tree(rng, t) for _ in range(batch)]).astype(np.int32)
+    if t > 1:  # some requests get several first-level nodes
+        for b in range(0, batch, 2):
+            parents[b, int(rng.integers(1, t))] = -1
+    tokens = np.zeros((batch, t), dtype=np.int32)
+    for b in range(batch):
+        for node in range(t):
+            sib = [int(tokens[b, j]) for j in range(node) if parents[b, j] == parents[b, node]]
+            while True:
+                tok = int(rng.integers(0, vocab))
+                if tok not in sib or len(sib) >= vocab:
+                    break
+            tokens[b, node] = tok
+    logits = rng.standard_normal((batch, t + 1, vocab), dtype=np.float32)
+    paths = []
+    for b in range(batch):
+        path = []
+        if plant:
+            leaf = int(rng.integers(0, t))
+            chain = [leaf]
+            while parents[b, chain[-1]] >= 0:
+                chain.append(int(parents[b, chain[-1]]))
+            chain = chain[::-1][:int(rng.integers(0, len(chain) + 1))]
+            prev_row = 0
+            for node in chain:
+                logits[b, prev_row, tokens[b, node]] += 20.0
+                prev_row = 1 + node
+            path = chain
+        paths.append(path)
+    return dict(name=f"accept_s{seed}", seed=seed, batch=batch, tree_nodes=t, vocab=vocab, tree_parent=parents,
+                draft_tokens=tokens, logits=logits, planted=paths)
