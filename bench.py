@@ -9,7 +9,9 @@ decode steps.  Prints one JSON line; see the design doc for the fields.
 
 With --op relocate it measures Tier-1 relocation instead: one call moves a 185,000-row
 prefix, scattered over the lower half of a 524,288-slot pool, into one run in the upper
-half (the index list is restored before each call, outside the timed region).
+half (the index list is restored before each call, outside the timed region).  With
+--op accept it measures greedy acceptance of a 64-node tree over fp32 logits of a
+131,072-token vocabulary.
 """
 
 from __future__ import annotations
@@ -235,6 +237,75 @@ def bench_relocate(args) -> int:
     return 0
 
 
+ACCEPT_B, ACCEPT_T, ACCEPT_V = 1, 64, 131072
+ACCEPT_METRIC = "tree-acceptance GB/s (fp32 logits read), 64-node tree, 131,072-token vocabulary"
+
+
+def bench_accept(args) -> int:
+    import torch
+
+    import mla_tree_verify_mlaverify_amd as mv
+    from workloads import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = synth.accept_config(0, batch=ACCEPT_B, tree_nodes=ACCEPT_T, vocab=ACCEPT_V)
+    logits = torch.from_numpy(cfg["logits"]).to(dev)
+    tokens = torch.from_numpy(cfg["draft_tokens"]).to(dev)
+    parents = torch.from_numpy(cfg["tree_parent"]).to(dev)
+    v = mv.Verifier(num_heads=1, max_batch=ACCEPT_B, max_tree_nodes=ACCEPT_T, max_prefix_len=1, pool_slots=1,
+                    device=dev)
+    flush = torch.zeros(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        if not args.warm:
+            flush.add_(1.0)
+        v.accept(logits, tokens, parents, stream=stream)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    wall0 = time.perf_counter()
+    for k in range(args.steps):
+        if not args.warm:
+            flush.add_(1.0)
+        starts[k].record(stream)
+        lens, _, _ = v.accept(logits, tokens, parents, stream=stream)
+        ends[k].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    assert v.read_device_errors() == 0
+    call_ms = [s_.elapsed_time(e) for s_, e in zip(starts, ends)]
+    med_ms = statistics.median(call_ms)
+    nbytes = ACCEPT_B * (ACCEPT_T + 1) * ACCEPT_V * 4
+    gbs = nbytes / (med_ms * 1e-3) / 1e9
+    line = {
+        "metric": ACCEPT_METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(med_ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp32", "data": "synthetic",
+        "config": {"workload": f"accept_b{ACCEPT_B}_t{ACCEPT_T}_v{ACCEPT_V}", "batch": ACCEPT_B,
+                   "tree_nodes": ACCEPT_T, "vocab": ACCEPT_V, "accepted": int(lens[0]),
+                   "cache": "warm" if args.warm else "flushed 1 GiB before each call"},
+        "us_per_call": {"median": round(med_ms * 1e3, 2), "p10": round(float(np.percentile(call_ms, 10)) * 1e3, 2),
+                        "p90": round(float(np.percentile(call_ms, 90)) * 1e3, 2)},
+        "wall_s_timed_loop": round(wall, 4),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "k_accept_* (one call)",
+                     "kernel_avg_us": round(1e3 * sum(call_ms) / len(call_ms), 2)},
+    }
+    if not args.no_cpu:
+        from oracle import accept_oracle as acc
+
+        t0 = time.perf_counter()
+        acc.accept(cfg["logits"], cfg["draft_tokens"], cfg["tree_parent"])
+        secs = time.perf_counter() - t0
+        line["cpu_baseline"] = {"value": round(nbytes / secs / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+                                "sample": f"one whole call on the same inputs ({secs:.3f} s); the oracle takes the argmax "
+                                          "only of the rows its walk visits, the GPU of every row",
+                                "cpu_model": lscpu_model()}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -246,7 +317,7 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--split", type=int, default=0, help="fixed split length (0 = automatic)")
-    ap.add_argument("--op", choices=("verify", "relocate"), default="verify")
+    ap.add_argument("--op", choices=("verify", "relocate", "accept"), default="verify")
     ap.add_argument("--page", type=int, default=0, help="prefix page size (block table of page ids); 0 = per token")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -254,6 +325,8 @@ def main() -> int:
         return 2
     if args.op == "relocate":
         return bench_relocate(args)
+    if args.op == "accept":
+        return bench_accept(args)
 
     import torch
 

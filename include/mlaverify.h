@@ -162,6 +162,31 @@ MLAVERIFY_API int mlaverify_relocate(mlaverify_t h, int32_t batch, int32_t tree_
                                      int32_t* kv_indices, const int32_t* prefix_lens, const int32_t* dst_start,
                                      void* stream);
 
+/* Greedy acceptance of a verified draft tree, the step that decides what a verify pass
+ * commits (the "Chunk 66.0" summary reports the resulting commit lengths, 7-8 tokens on
+ * predictable text).  Rule, per request: start at the position before the tree; take the
+ * argmax g of the current logits row; move to the lowest-index child (a node with parent
+ * -1 at the start) whose draft token is g, and repeat from its row; stop when no child
+ * matches.  The bonus token is the argmax of the last row visited, so the step commits
+ * accept_len + 1 tokens.  argmax: largest value, lowest index among equal values, NaN
+ * ranked below every number (a row of NaN gives 0), -0 equal to +0.
+ * Host arguments: batch in [1, max_batch], tree_nodes (T) in [1, max_tree_nodes],
+ * vocab >= 1.  Device arguments:
+ *   logits       fp32 [batch, T + 1, vocab]: row 0 at the position before the tree, row
+ *                1 + i after tree node i (read)
+ *   draft_tokens int32 [batch, T]: the token drafted at each node (read)
+ *   tree_parent  int32 [batch, T], as for mlaverify_run (read)
+ *   accept_len   int32 [batch] (written): nodes accepted
+ *   accepted     int32 [batch, T] (written): the accepted nodes in path order, then -1
+ *   bonus        int32 [batch] (written)
+ * A request whose tree has a parent outside [-1, node) accepts nothing (its bonus token is
+ * row 0's argmax) and sets MLAVERIFY_DEVERR_BAD_PARENT.  The caller owns every buffer; the
+ * call uses the handle's workspace (ordered with run on one stream), never synchronises,
+ * copies to the host or allocates: graph-capturable. */
+MLAVERIFY_API int mlaverify_accept(mlaverify_t h, int32_t batch, int32_t tree_nodes, int32_t vocab,
+                                   const float* logits, const int32_t* draft_tokens, const int32_t* tree_parent,
+                                   int32_t* accept_len, int32_t* accepted, int32_t* bonus, void* stream);
+
 /* Builds the tree-ancestor bitmasks alone (the mask step of run, on its own):
  * masks[b*T + i] bit j is set iff tree node j is node i or one of its ancestors.
  * tree_parent int32 [batch, T] and masks uint64 [batch, T] are device pointers;

@@ -43,6 +43,7 @@ EXPORTED = (
     "mlaverify_create",
     "mlaverify_run",
     "mlaverify_relocate",
+    "mlaverify_accept",
     "mlaverify_tree_masks",
     "mlaverify_read_plan",
     "mlaverify_read_device_errors",
@@ -99,6 +100,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.mlaverify_run.restype = ctypes.c_int
     lib.mlaverify_relocate.argtypes = [c_void_p, c_int32, c_int32] + [c_void_p] * 5
     lib.mlaverify_relocate.restype = ctypes.c_int
+    lib.mlaverify_accept.argtypes = [c_void_p, c_int32, c_int32, c_int32] + [c_void_p] * 7
+    lib.mlaverify_accept.restype = ctypes.c_int
     lib.mlaverify_tree_masks.argtypes = [c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p]
     lib.mlaverify_tree_masks.restype = ctypes.c_int
     lib.mlaverify_read_plan.argtypes = [c_void_p, c_int32, c_void_p, ctypes.POINTER(c_int32), c_int32]
@@ -244,6 +247,28 @@ class Verifier:
                                          prefix_lens.data_ptr(), dst_start.data_ptr(), _stream_handle(stream))
         if rc != OK:
             raise MlaVerifyError(rc, "mlaverify_relocate")
+
+    def accept(self, logits, draft_tokens, tree_parent, stream=None):
+        """Greedy acceptance of a verified tree; returns (accept_len [B], accepted [B, T], bonus [B]).
+        Invalid trees show in read_device_errors."""
+        dev = self.device
+        if tree_parent.dim() != 2:
+            raise ValueError("tree_parent must be [batch, T]")
+        b, t = tree_parent.shape
+        _check(tree_parent, "tree_parent", torch.int32, (b, t), dev)
+        _check(draft_tokens, "draft_tokens", torch.int32, (b, t), dev)
+        if logits.dim() != 3 or logits.shape[0] != b or logits.shape[1] != t + 1:
+            raise ValueError(f"logits must be [batch, T + 1, vocab] = [{b}, {t + 1}, V]")
+        _check(logits, "logits", torch.float32, None, dev)
+        accept_len = torch.empty(b, dtype=torch.int32, device=dev)
+        accepted = torch.empty((b, t), dtype=torch.int32, device=dev)
+        bonus = torch.empty(b, dtype=torch.int32, device=dev)
+        rc = self.lib.mlaverify_accept(self.handle, b, t, logits.shape[2], logits.data_ptr(), draft_tokens.data_ptr(),
+                                       tree_parent.data_ptr(), accept_len.data_ptr(), accepted.data_ptr(),
+                                       bonus.data_ptr(), _stream_handle(stream))
+        if rc != OK:
+            raise MlaVerifyError(rc, "mlaverify_accept")
+        return accept_len, accepted, bonus
 
     def read_plan(self, batch: int | None = None, stream=None) -> dict:
         """Work partition of the last run (synchronises the stream)."""

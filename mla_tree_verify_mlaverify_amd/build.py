@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libmlaverify.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
-SOURCES = ("api.hip", "kernels.hip", "relocate.hip")
+SOURCES = ("api.hip", "kernels.hip", "relocate.hip", "accept.hip")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

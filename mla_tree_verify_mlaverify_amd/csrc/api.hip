@@ -36,7 +36,7 @@ int units_for(const mlaverify_config& c, int batch, int T) {
 }
 
 struct Layout {
-  size_t hdr, req, unit_tab, masks, part_lse, part_o, reloc_off, reloc_status, reloc_maps, total;
+  size_t hdr, req, unit_tab, masks, part_lse, part_o, reloc_off, reloc_status, reloc_maps, accept_keys, total;
   int units_cap;      // entries of unit_tab
   int64_t rows_cap;   // rows of part_o / part_lse
 };
@@ -63,6 +63,8 @@ Layout layout_for(const mlaverify_config& c) {
   // relocation: segment offsets, refusal word, a bitmap and a byte map over the pool slots
   L.reloc_off = off;    off = align_up(off + sizeof(int32_t) * (size_t)c.max_batch);
   L.reloc_status = off; off = align_up(off + sizeof(uint32_t));
+  // acceptance: argmax keys, zero between calls
+  L.accept_keys = off;  off = align_up(off + sizeof(uint64_t) * (size_t)c.max_batch * (c.max_tree_nodes + 1));
   L.reloc_maps = off;   off = align_up(off + sizeof(uint32_t) * (size_t)(cdiv(c.pool_slots, 32) + cdiv(c.pool_slots, 4)));
   L.total = off;
   return L;
@@ -151,8 +153,11 @@ int mlaverify_create(const mlaverify_config* c, void* workspace, size_t workspac
     hd->ws = static_cast<char*>(workspace);
     hd->ws_bytes = workspace_bytes;
   }
-  // Clear the plan header (sticky error word) once; run never needs a memset.
-  if (hipMemset(hd->ws + L.hdr, 0, sizeof(PlanHeader)) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+  // Clear the plan header (sticky error word) and the acceptance keys once;
+  // no call needs a memset afterwards (acceptance leaves its area at zero).
+  if (hipMemset(hd->ws + L.hdr, 0, sizeof(PlanHeader)) != hipSuccess ||
+      hipMemset(hd->ws + L.accept_keys, 0, L.reloc_maps - L.accept_keys) != hipSuccess ||
+      hipDeviceSynchronize() != hipSuccess) {
     if (hd->owns_ws) (void)hipFree(hd->ws);
     delete hd;
     return MLAVERIFY_ERR_HIP;
@@ -254,6 +259,35 @@ int mlaverify_relocate(mlaverify_t hd, int32_t batch, int32_t T, void* kv_pool, 
   a.T = T;
   a.max_prefix = c.max_prefix_len;
   if (launch_relocate(a, static_cast<hipStream_t>(stream)) != hipSuccess) return MLAVERIFY_ERR_HIP;
+  return MLAVERIFY_OK;
+}
+
+int mlaverify_accept(mlaverify_t hd, int32_t batch, int32_t T, int32_t vocab, const float* logits,
+                     const int32_t* draft_tokens, const int32_t* tree_parent, int32_t* accept_len, int32_t* accepted,
+                     int32_t* bonus, void* stream) {
+  if (!hd) return MLAVERIFY_ERR_INVALID_ARG;
+  const mlaverify_config& c = hd->cfg;
+  if (batch < 1 || batch > c.max_batch || T < 1 || T > c.max_tree_nodes || vocab < 1) return MLAVERIFY_ERR_INVALID_ARG;
+  if (!logits || !draft_tokens || !tree_parent || !accept_len || !accepted || !bonus) return MLAVERIFY_ERR_INVALID_ARG;
+  if (!aligned(logits, 4) || !aligned(draft_tokens, 4) || !aligned(tree_parent, 4) || !aligned(accept_len, 4) ||
+      !aligned(accepted, 4) || !aligned(bonus, 4))
+    return MLAVERIFY_ERR_INVALID_ARG;
+  AcceptArgs a;
+  a.logits = logits;
+  a.draft_tokens = draft_tokens;
+  a.tree_parent = tree_parent;
+  a.accept_len = accept_len;
+  a.accepted = accepted;
+  a.bonus = bonus;
+  a.keys = reinterpret_cast<uint64_t*>(hd->ws + hd->L.accept_keys);
+  a.sticky_err = &reinterpret_cast<PlanHeader*>(hd->ws + hd->L.hdr)->sticky_err;
+  a.vocab = vocab;
+  a.batch = batch;
+  a.T = T;
+  a.rows = batch * (T + 1);
+  a.chunks = accept_chunks(vocab);
+  if ((int64_t)a.rows * a.chunks > INT32_MAX) return MLAVERIFY_ERR_UNSUPPORTED;
+  if (launch_accept(a, static_cast<hipStream_t>(stream)) != hipSuccess) return MLAVERIFY_ERR_HIP;
   return MLAVERIFY_OK;
 }
 

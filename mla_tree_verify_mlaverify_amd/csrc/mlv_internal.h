@@ -101,8 +101,24 @@ struct RelocArgs {
   int batch, T, max_prefix;
 };
 
-// Launchers (kernels.hip, relocate.hip).
+// Greedy acceptance of a verified tree (accept.hip).
+struct AcceptArgs {
+  const float* logits;         // [batch, T + 1, vocab]
+  const int32_t* draft_tokens; // [batch, T]
+  const int32_t* tree_parent;  // [batch, T]
+  int32_t* accept_len;         // [batch]
+  int32_t* accepted;           // [batch, T]
+  int32_t* bonus;              // [batch]
+  uint64_t* keys;              // [rows] argmax key per logits row (workspace, zero between calls)
+  uint32_t* sticky_err;
+  int64_t vocab;
+  int batch, T, rows, chunks;  // rows = batch * (T + 1); chunks = argmax workgroups per row
+};
+
+// Launchers (kernels.hip, relocate.hip, accept.hip).
 hipError_t launch_relocate(const RelocArgs& a, hipStream_t s);
+hipError_t launch_accept(const AcceptArgs& a, hipStream_t s);
+int accept_chunks(int64_t vocab);
 hipError_t launch_partial(const PartialArgs& a, int grid, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
 hipError_t launch_tree_masks(const int32_t* tree_parent, int batch, int T, uint64_t* masks, uint32_t* err,
