@@ -90,6 +90,19 @@ def ancestor_masks(parents) -> np.ndarray:
     return masks
 
 
+def ancestor_mask_words(parents) -> np.ndarray:
+    """The same masks for any T, as ceil(T / 64) uint64 words per node: bit j % 64 of word
+    j // 64 of row i is set iff node j is in anc*(i)."""
+    parents = np.asarray(parents)
+    t = len(parents)
+    validate_parents(parents)
+    words = np.zeros((t, -(-t // 64)), dtype=np.uint64)
+    for i in range(t):
+        for a in ancestors_with_self(parents, i):
+            words[i, a // 64] |= np.uint64(1 << (a % 64))
+    return words
+
+
 def request_offsets(prefix_lens, tree_nodes: int) -> np.ndarray:
     """off_b: start of request b's segment in kv_indices (exclusive prefix sum of P_b + T)."""
     offs = np.zeros(len(prefix_lens), dtype=np.int64)

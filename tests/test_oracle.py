@@ -112,6 +112,24 @@ def test_masks_match_transitive_closure(seed, kind):
         assert int(masks[i]) >> t == 0
 
 
+@pytest.mark.parametrize("t,kind", [(65, "chain"), (100, "random"), (128, "forest"), (200, "random"),
+                                    (256, "chain"), (256, "forest")])
+def test_mask_words_match_transitive_closure(t, kind):
+    rng = np.random.default_rng(t)
+    if kind == "random":
+        parents = synth.random_tree(rng, t)
+    elif kind == "chain":
+        parents = synth.chain_tree(t)
+    else:
+        parents = np.array([int(rng.integers(-1, i)) for i in range(t)], dtype=np.int32)
+    words = orc.ancestor_mask_words(parents)
+    assert words.shape == (t, -(-t // 64))
+    reach = closure_masks(parents)
+    for i in range(t):
+        bits = [(int(words[i, j // 64]) >> (j % 64)) & 1 for j in range(64 * words.shape[1])]
+        assert bits[:t] == reach[i].astype(int).tolist() and not any(bits[t:])
+
+
 def test_invalid_parent_rejected():
     with pytest.raises(ValueError):
         orc.ancestor_masks(np.array([-1, 0, 2]))  # node 2 is its own parent
