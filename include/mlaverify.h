@@ -49,7 +49,7 @@ extern "C" {
 
 #define MLAVERIFY_LATENT_DIM 576 /* columns of a KV row used for scores */
 #define MLAVERIFY_V_DIM 512      /* leading columns of a KV row used as V */
-#define MLAVERIFY_MAX_TREE_NODES 64
+#define MLAVERIFY_MAX_TREE_NODES 256
 
 /* Status codes. */
 #define MLAVERIFY_OK 0
@@ -76,7 +76,8 @@ typedef struct mlaverify_handle* mlaverify_t;
 typedef struct mlaverify_config {
   int32_t num_heads;       /* H: heads of this rank, 1..128 */
   int32_t max_batch;       /* largest batch passed to run; sizes the grid and workspace */
-  int32_t max_tree_nodes;  /* largest T passed to run, 1..64 (one 64-bit ancestor mask per node) */
+  int32_t max_tree_nodes;  /* largest T passed to run, 1..256 (trees over 64 nodes use a
+                              kernel variant with four 64-bit mask words per node) */
   int32_t max_prefix_len;  /* largest P_b accepted; larger ones are device errors */
   int64_t pool_slots;      /* rows in kv_pool; indices outside [0, pool_slots) are device errors */
   int64_t kv_row_stride;   /* elements between consecutive pool rows, >= 576, multiple of 8 */
@@ -187,11 +188,12 @@ MLAVERIFY_API int mlaverify_accept(mlaverify_t h, int32_t batch, int32_t tree_no
                                    const float* logits, const int32_t* draft_tokens, const int32_t* tree_parent,
                                    int32_t* accept_len, int32_t* accepted, int32_t* bonus, void* stream);
 
-/* Builds the tree-ancestor bitmasks alone (the mask step of run, on its own):
- * masks[b*T + i] bit j is set iff tree node j is node i or one of its ancestors.
- * tree_parent int32 [batch, T] and masks uint64 [batch, T] are device pointers;
+/* Builds the tree-ancestor bitmasks alone (the mask step of run, on its own), as
+ * W = ceil(T / 64) words per node: bit j % 64 of masks[(b*T + i)*W + j / 64] is set iff
+ * tree node j is node i or one of its ancestors.
+ * tree_parent int32 [batch, T] and masks uint64 [batch, T, W] are device pointers;
  * err (device, uint32 [batch]) receives MLAVERIFY_DEVERR_BAD_PARENT per bad
- * request, whose masks are then 0.  1 <= T <= 64.  Enqueued on `stream`. */
+ * request, whose masks are then 0.  1 <= T <= 256.  Enqueued on `stream`. */
 MLAVERIFY_API int mlaverify_tree_masks(const int32_t* tree_parent, int32_t batch, int32_t tree_nodes,
                                        uint64_t* masks, uint32_t* err, void* stream);
 

@@ -20,7 +20,7 @@ LIB_PATH = os.environ.get("MLAVERIFY_LIBRARY") or os.path.join(_PKG_DIR, "libmla
 
 LATENT_DIM = 576
 V_DIM = 512
-MAX_TREE_NODES = 64
+MAX_TREE_NODES = 256
 
 OK = 0
 ERR_INVALID_ARG = -1
@@ -309,13 +309,14 @@ class Verifier:
 
 
 def tree_masks(tree_parent: torch.Tensor, stream=None):
-    """Ancestor-or-self bitmasks on the GPU: returns (masks int64 [B, T] holding the uint64 bits, err int32 [B])."""
+    """Ancestor-or-self bitmasks on the GPU: returns (masks int64 [B, T, ceil(T/64)] holding the uint64
+    words, err int32 [B])."""
     lib = load_library()
     if tree_parent.dim() != 2:
         raise ValueError("tree_parent must be [batch, T]")
     b, t = tree_parent.shape
     _check(tree_parent, "tree_parent", torch.int32, (b, t))
-    masks = torch.empty((b, t), dtype=torch.int64, device=tree_parent.device)
+    masks = torch.empty((b, t, (t + 63) // 64), dtype=torch.int64, device=tree_parent.device)
     err = torch.empty((b,), dtype=torch.int32, device=tree_parent.device)
     rc = lib.mlaverify_tree_masks(tree_parent.data_ptr(), b, t, masks.data_ptr(), err.data_ptr(),
                                   _stream_handle(stream))

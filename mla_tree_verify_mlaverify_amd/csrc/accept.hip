@@ -51,35 +51,53 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
   return x;
 }
 
-// Tree walk of request b from its argmax keys (one wave).
+// Tree walk of request b from its argmax keys (one wave; lane l holds nodes l, l + 64, ...).
 __device__ void accept_walk(const AcceptArgs& a, int b) {
+  constexpr int G = kMaxTree / 64;  // node groups per lane
   const int lane = threadIdx.x, T = a.T;
-  const bool node = lane < T;
-  const int par = node ? a.tree_parent[(int64_t)b * T + lane] : -2;
-  const int tok = node ? a.draft_tokens[(int64_t)b * T + lane] : -1;
-  const bool bad = __any(node && (par < -1 || par >= lane));
+  int par[G], tok[G], mine[G];
+  bool bad = false;
+#pragma unroll
+  for (int k = 0; k < G; k++) {
+    const int i = lane + 64 * k;
+    par[k] = i < T ? a.tree_parent[(int64_t)b * T + i] : -2;
+    tok[k] = i < T ? a.draft_tokens[(int64_t)b * T + i] : -1;
+    bad |= i < T && (par[k] < -1 || par[k] >= i);
+    mine[k] = -1;
+  }
+  bad = __any(bad);
   uint64_t* krow = a.keys + (int64_t)b * (T + 1);
   // keys were merged with atomics: read them at device scope
   auto token_of = [&](int row) -> int {
     const uint64_t k = __hip_atomic_load(krow + row, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return (int)(0xFFFFFFFFu - (uint32_t)k);
   };
-  int cur = -1, row = 0, n = 0, mine = -1;
+  int cur = -1, row = 0, n = 0;
   if (!bad) {
     // the next node has a larger index than the current one, so at most T steps
     for (int step = 0; step < T; step++) {
       const int g = token_of(row);
-      const uint64_t m = __ballot(node && par == cur && tok == g);
-      if (m == 0ull) break;
-      const int nxt = __builtin_ctzll(m);
-      if (lane == n) mine = nxt;
+      int nxt = -1;
+#pragma unroll
+      for (int k = G - 1; k >= 0; k--) {  // lowest matching node: the first group that has one
+        const uint64_t m = __ballot(par[k] == cur && tok[k] == g);
+        if (m) nxt = 64 * k + __builtin_ctzll(m);
+      }
+      if (nxt < 0) break;
+#pragma unroll
+      for (int k = 0; k < G; k++)
+        if (lane + 64 * k == n) mine[k] = nxt;
       n++;
       cur = nxt;
       row = 1 + nxt;
     }
   }
   const int g = token_of(row);
-  if (node) a.accepted[(int64_t)b * T + lane] = lane < n ? mine : -1;
+#pragma unroll
+  for (int k = 0; k < G; k++) {
+    const int i = lane + 64 * k;
+    if (i < T) a.accepted[(int64_t)b * T + i] = i < n ? mine[k] : -1;
+  }
   if (lane == 0) {
     a.accept_len[b] = n;
     a.bonus[b] = g;

@@ -36,7 +36,7 @@ int units_for(const mlaverify_config& c, int batch, int T) {
 }
 
 struct Layout {
-  size_t hdr, req, unit_tab, masks, part_lse, part_o, reloc_off, reloc_status, reloc_maps, accept_keys, total;
+  size_t hdr, req, unit_tab, part_lse, part_o, reloc_off, reloc_status, reloc_maps, accept_keys, total;
   int units_cap;      // entries of unit_tab
   int64_t rows_cap;   // rows of part_o / part_lse
 };
@@ -57,7 +57,6 @@ Layout layout_for(const mlaverify_config& c) {
   L.hdr = off;       off = align_up(off + sizeof(PlanHeader));
   L.req = off;       off = align_up(off + sizeof(ReqPlan) * (size_t)c.max_batch);
   L.unit_tab = off;  off = align_up(off + sizeof(int32_t) * (size_t)units_cap);
-  L.masks = off;     off = align_up(off + sizeof(uint64_t) * (size_t)c.max_batch * c.max_tree_nodes);
   L.part_lse = off;  off = align_up(off + sizeof(float) * (size_t)rows_cap);
   L.part_o = off;    off = align_up(off + sizeof(uint16_t) * (size_t)rows_cap * kVdim);  // bf16
   // relocation: segment offsets, refusal word, a bitmap and a byte map over the pool slots

@@ -35,33 +35,62 @@ typedef __attribute__((address_space(1))) const void gmem_cvoid;
 typedef __attribute__((address_space(3))) void lds_void;
 
 // ------------------------------------------------------------------------------------------
-// Ancestor-or-self bitmask of tree node i: bit j set iff j == i or j is an ancestor of i.
-// Parents must satisfy -1 <= parent[j] < j; the walk stops (and reports) on the first
-// violation, so it always terminates and never reads outside par[0..i].
-__device__ __forceinline__ uint64_t ancestor_mask(const int32_t* __restrict__ par, int i, bool& bad) {
-  uint64_t m = 0;
-  int p = i;
-  while (p >= 0) {
-    m |= 1ull << p;
-    const int pp = par[p];
-    if (pp < -1 || pp >= p) {
-      bad = true;
-      return 0;
-    }
-    p = pp;
+// Ancestor-or-self bitmasks of the T nodes of one tree (row a.1): bit j of node i's mask
+// (word j / 64 of W) is set iff j == i or j is an ancestor of i.  Pointer jumping in LDS:
+// after round r, node i holds its ancestors at distance < 2^r and points at the one at
+// distance 2^r, so ceil(log2 T) rounds suffice whatever the depth.  Thread i < T owns node
+// i (the workgroup has at least T threads); s_m holds T x W words, s_jump T ints.  Parents
+// must satisfy -1 <= parent[i] < i; the result says whether one does not (then the masks
+// are not meaningful).  Called by every thread of the workgroup.
+template <int W>
+__device__ bool build_masks(const int32_t* __restrict__ par, int T, uint64_t* s_m, int* s_jump) {
+  const int i = threadIdx.x;
+  int jmp = -1;
+  bool bad = false;
+  if (i < T) {
+    const int p = par[i];
+    bad = p < -1 || p >= i;
+    jmp = bad ? -1 : p;
+#pragma unroll
+    for (int w = 0; w < W; w++) s_m[i * W + w] = (w == (i >> 6)) ? 1ull << (i & 63) : 0ull;
+    s_jump[i] = jmp;
   }
-  return m;
+  const bool any_bad = __syncthreads_or(bad) != 0;
+  for (int span = 1; span < T; span <<= 1) {
+    uint64_t add[W];
+    int nj = -1;
+#pragma unroll
+    for (int w = 0; w < W; w++) add[w] = 0ull;
+    if (i < T && jmp >= 0) {
+#pragma unroll
+      for (int w = 0; w < W; w++) add[w] = s_m[jmp * W + w];
+      nj = s_jump[jmp];
+    }
+    __syncthreads();
+    if (i < T && jmp >= 0) {
+#pragma unroll
+      for (int w = 0; w < W; w++) s_m[i * W + w] |= add[w];
+      s_jump[i] = nj;
+      jmp = nj;
+    }
+    __syncthreads();
+  }
+  return any_bad;
 }
 
-__global__ __launch_bounds__(64) void k_tree_masks(const int32_t* __restrict__ par, int T,
-                                                    uint64_t* __restrict__ masks, uint32_t* __restrict__ err) {
+// Standalone mask step: one workgroup per request writes masks[b][i][0 .. ceil(T/64) - 1].
+__global__ __launch_bounds__(kThreads) void k_tree_masks(const int32_t* __restrict__ par, int T,
+                                                         uint64_t* __restrict__ masks, uint32_t* __restrict__ err) {
+  __shared__ uint64_t s_m[kMaxTree * kMaxTreeWords];
+  __shared__ int s_jump[kMaxTree];
   const int b = blockIdx.x, i = threadIdx.x;
-  bool bad = false;
-  uint64_t m = 0;
-  if (i < T) m = ancestor_mask(par + (size_t)b * T, i, bad);
-  const bool any_bad = __any(bad);
-  if (i < T) masks[(size_t)b * T + i] = any_bad ? 0ull : m;
-  if (i == 0) err[b] = any_bad ? kErrBadParent : 0u;
+  const bool bad = build_masks<kMaxTreeWords>(par + (size_t)b * T, T, s_m, s_jump);
+  const int W = (T + 63) >> 6;
+  for (int k = i; k < T * W; k += kThreads) {
+    const int node = k / W, w = k - node * W;
+    masks[(size_t)b * T * W + k] = bad ? 0ull : s_m[node * kMaxTreeWords + w];
+  }
+  if (i == 0) err[b] = bad ? kErrBadParent : 0u;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -336,16 +365,15 @@ __device__ int plan_units(const PartialArgs& a, int g, bool publish, int* s_tmp,
 }
 
 // kPaged: the prefix is addressed through a block table of 2^page_log2-slot pages (the
-// index segment holds page ids); otherwise through one slot per token.
-template <bool kPaged>
+// index segment holds page ids); otherwise through one slot per token.  kBigTree: T > 64,
+// so a row's ancestor mask takes kMaxTreeWords 64-bit words instead of one.
+template <bool kPaged, bool kBigTree>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_partial(PartialArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[kTileBufs * kTileBytes + kWaves * kQLdsBytes];
   __shared__ int s_restart[2][kWaves];
   __shared__ int s_tmp[kWaves];
   __shared__ int s_unit[8];
-  __shared__ uint64_t s_masks[kMaxTree];
-  __shared__ int s_badpar;
   lds_char* lds = (lds_char*)smem;
 
   const int tid = threadIdx.x;
@@ -361,7 +389,6 @@ void k_partial(PartialArgs a) {
   const int slot = bid >> 3;
   const int mt = slot % a.n_mtiles;
   const int g = (slot / a.n_mtiles) * 8 + (bid & 7);
-  if (tid == 0) s_badpar = 0;
   const int total_units = plan_units(a, g, g == 0 && mt == 0, s_tmp, s_unit);
   if (g >= total_units || g >= a.units_cap) return;
   const int b = s_unit[0];
@@ -389,14 +416,13 @@ void k_partial(PartialArgs a) {
   };
 
   // Tree-ancestor bitmasks of this request (row a.1), for the unit that covers the tree.
+  // They are built in tile buffer 2, which no gather writes before the loop's first
+  // iteration, and each row copies its own mask into registers before that.
+  constexpr int kW = kBigTree ? kMaxTreeWords : 1;
+  uint64_t* s_m = reinterpret_cast<uint64_t*>(smem + 2 * kTileBytes);
   if (last) {
-    if (tid < a.T) {
-      bool bad = false;
-      s_masks[tid] = ancestor_mask(a.tree_parent + (size_t)b * a.T, tid, bad);
-      if (bad) s_badpar = 1;
-    }
-    __syncthreads();
-    if (s_badpar) {
+    int* s_jump = reinterpret_cast<int*>(smem + 2 * kTileBytes + kMaxTree * kMaxTreeWords * 8);
+    if (build_masks<kW>(a.tree_parent + (size_t)b * a.T, a.T, s_m, s_jump)) {
       req_err |= kErrBadParent;
       if (tid == 0 && mt == 0) atomicOr(a.sticky_err, kErrBadParent);
     }
@@ -439,7 +465,9 @@ void k_partial(PartialArgs a) {
 #pragma unroll
     for (int kk = kQReg; kk < 36; kk++) qlds[(kk - kQReg) * 64] = qp[2 * kk];
   }
-  const uint64_t anc = (last && rvalid) ? s_masks[r / a.H] : ~0ull;
+  uint64_t anc[kW];
+#pragma unroll
+  for (int w = 0; w < kW; w++) anc[w] = (last && rvalid) ? s_m[(r / a.H) * kW + w] : ~0ull;
 
   // Gather geometry: thread tid loads 9 chunks of key kt of every tile.
   const int kt = tid >> 3;
@@ -707,7 +735,11 @@ void k_partial(PartialArgs a) {
     const int tt = t - npt;
     const int nv = tree ? min(kTileKeys, a.T - tt * kTileKeys) : min(kTileKeys, npk - t * kTileKeys);
     if (__builtin_expect(tree || nv < kTileKeys, 0)) {
-      const uint32_t tm = (uint32_t)((tree ? (anc >> (tt * kTileKeys)) : ~0ull) >> (4 * h));
+      uint64_t aw = anc[0];  // the word holding tree tile tt's 32 keys
+#pragma unroll
+      for (int w = 1; w < kW; w++) aw = (tt >> 1) == w ? anc[w] : aw;
+      const uint32_t win = tree ? (uint32_t)(aw >> ((tt & 1) * kTileKeys)) : ~0u;
+      const uint32_t tm = win >> (4 * h);
       const int nvh = nv - 4 * h;
 #pragma unroll
       for (int v = 0; v < 16; v++) {
@@ -882,10 +914,15 @@ __global__ __launch_bounds__(256) void k_merge(MergeArgs a) {
 
 // ------------------------------------------------------------------------------------------
 hipError_t launch_partial(const PartialArgs& a, int grid, hipStream_t s) {
-  if (a.page_log2 > 0)
-    hipLaunchKernelGGL(k_partial<true>, dim3(grid), dim3(kThreads), 0, s, a);
+  const bool paged = a.page_log2 > 0, big = a.T > 64;
+  if (paged && big)
+    hipLaunchKernelGGL((k_partial<true, true>), dim3(grid), dim3(kThreads), 0, s, a);
+  else if (paged)
+    hipLaunchKernelGGL((k_partial<true, false>), dim3(grid), dim3(kThreads), 0, s, a);
+  else if (big)
+    hipLaunchKernelGGL((k_partial<false, true>), dim3(grid), dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL(k_partial<false>, dim3(grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((k_partial<false, false>), dim3(grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -904,7 +941,7 @@ hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
 
 hipError_t launch_tree_masks(const int32_t* tree_parent, int batch, int T, uint64_t* masks, uint32_t* err,
                              hipStream_t s) {
-  hipLaunchKernelGGL(k_tree_masks, dim3(batch), dim3(64), 0, s, tree_parent, T, masks, err);
+  hipLaunchKernelGGL(k_tree_masks, dim3(batch), dim3(kThreads), 0, s, tree_parent, T, masks, err);
   return hipGetLastError();
 }
 

@@ -21,7 +21,10 @@ constexpr int kMergeDepth = 8;                        // partial loads in flight
 constexpr int kMergeBlocks = 2048;                     // merge grid target: rows x column split
 constexpr int kTileBufs = 3;                           // KV tiles in LDS: tile t, t+1 (in use), t+2 (landing)
 constexpr int kQLdsBytes = (36 - kQReg) * 64 * 16;      // per-wave LDS slice for the other k-steps
-constexpr int kMaxTree = 64;
+constexpr int kMaxTree = 256;          // tree nodes per request (one thread per node builds the masks)
+constexpr int kMaxTreeWords = kMaxTree / 64;  // 64-bit ancestor-mask words per node
+static_assert(kMaxTree <= 64 * 4, "the mask builder has one thread per node");
+static_assert(kMaxTree * kMaxTreeWords * 8 + kMaxTree * 4 <= kTileBytes, "mask scratch fits one tile buffer");
 constexpr int kMaxPage = 1024;         // largest prefix page (block-table) size in slots
 constexpr int kMaxBatch = 1024;        // one plan thread per request
 constexpr int kTargetBlocks = 256;     // workgroups the split aims for (one per CU on MI355X)

@@ -48,7 +48,9 @@ def base_cfg(**kw):
 
 @pytest.mark.parametrize("kw,expect", [
     ({}, binding.OK),
-    (dict(max_tree_nodes=65), binding.ERR_UNSUPPORTED),
+    (dict(max_tree_nodes=65), binding.OK),
+    (dict(max_tree_nodes=256), binding.OK),
+    (dict(max_tree_nodes=257), binding.ERR_UNSUPPORTED),
     (dict(max_tree_nodes=0), binding.ERR_INVALID_ARG),
     (dict(num_heads=0), binding.ERR_INVALID_ARG),
     (dict(num_heads=129), binding.ERR_INVALID_ARG),

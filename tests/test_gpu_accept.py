@@ -39,7 +39,7 @@ def check(cfg, **kw):
 
 @pytest.mark.parametrize("seed,b,t,vocab", [
     (0, 1, 1, 1), (1, 1, 8, 16), (2, 4, 33, 1000), (3, 3, 17, 1003), (4, 8, 64, 131072), (5, 2, 64, 50001),
-    (6, 16, 5, 7), (7, 1, 64, 16384), (8, 2, 40, 16388),
+    (6, 16, 5, 7), (7, 1, 64, 16384), (8, 2, 40, 16388), (9, 2, 200, 5000), (10, 1, 256, 1000), (11, 3, 65, 64),
 ])
 def test_accept_matches_oracle(seed, b, t, vocab):
     cfg = synth.accept_config(seed, batch=b, tree_nodes=t, vocab=vocab)

@@ -24,7 +24,7 @@ pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not torch.cuda.is_available(),
 @pytest.mark.parametrize("seed", range(4))
 def test_tree_masks_bit_exact(seed):
     rng = np.random.default_rng(seed)
-    for t in (1, 2, 7, 8, 31, 32, 33, 63, 64):
+    for t in (1, 2, 7, 8, 31, 32, 33, 63, 64, 65, 100, 128, 129, 200, 255, 256):
         trees = [synth.random_tree(rng, t), synth.chain_tree(t),
                  np.array([int(rng.integers(-1, i)) for i in range(t)], dtype=np.int32)]
         par = np.stack(trees).astype(np.int32)
@@ -32,7 +32,9 @@ def test_tree_masks_bit_exact(seed):
         torch.cuda.synchronize()
         got = masks.cpu().numpy().view(np.uint64)
         for b in range(len(trees)):
-            assert np.array_equal(got[b], orc.ancestor_masks(par[b])), (t, b)
+            assert np.array_equal(got[b], orc.ancestor_mask_words(par[b])), (t, b)
+            if t <= 64:
+                assert np.array_equal(got[b][:, 0], orc.ancestor_masks(par[b]))
         assert np.all(err.cpu().numpy() == 0)
 
 
@@ -41,7 +43,7 @@ def test_tree_masks_flag_bad_parents():
     masks, err = mv.tree_masks(i32(par))
     torch.cuda.synchronize()
     e = err.cpu().numpy()
-    m = masks.cpu().numpy().view(np.uint64)
+    m = masks.cpu().numpy().view(np.uint64)[:, :, 0]
     assert e.tolist() == [0, mv.DEVERR_BAD_PARENT, mv.DEVERR_BAD_PARENT, mv.DEVERR_BAD_PARENT, mv.DEVERR_BAD_PARENT]
     assert np.array_equal(m[0], orc.ancestor_masks(par[0]))
     assert np.all(m[1:] == 0)
@@ -67,6 +69,13 @@ SMALL = [
     (12, [64] * 300, 2, 2, "random", 0),
     (13, [5] * 1024, 1, 1, "chain", 0),
     (14, [0] * 1000 + [4097], 3, 8, "random", 0),
+    # trees over 64 nodes: four mask words per row, up to 8 tree tiles in the last unit
+    (15, [700], 65, 8, "random", 0),
+    (16, [300, 1200], 100, 4, "forest", 256),
+    (17, [1000], 128, 8, "chain", 0),
+    (18, [2000], 256, 8, "random", 0),
+    (19, [0, 513], 200, 2, "chain", 0),
+    (20, [129], 256, 1, "forest", 64),
 ]
 
 
@@ -134,6 +143,28 @@ def test_column_scales_keep_per_column_precision():
     ref_out, ref_lse = run_oracle(cfg)
     s = synth.column_scales()
     print(compare(out / s, lse, ref_out / s, ref_lse))
+
+
+def test_ragged_trees_by_padding():
+    """Requests with 5 and 70 nodes in one call: the smaller tree is padded to 70 nodes with
+    extra roots (their own tree slots); the real nodes' rows must equal the oracle's for
+    the unpadded trees."""
+    rng = np.random.default_rng(31)
+    cfg = synth.small_config(31, batch=2, prefix=[400, 900], tree_nodes=70, heads=4, slots=8192)
+    par = cfg["tree_parent"].copy()
+    small = synth.random_tree(rng, 5)
+    par[0, :5] = small
+    par[0, 5:] = -1  # padding: extra roots, seen by nobody else
+    cfg["tree_parent"] = par
+    out, lse, _ = run_gpu(cfg)
+    ref_out, ref_lse = run_oracle(cfg)
+    # the oracle of request 0 alone, with its real 5-node tree
+    seg0 = cfg["kv_indices"][:400 + 70]
+    solo_idx = np.concatenate([seg0[:400], seg0[400:405]])
+    solo_out, solo_lse = orc.verify_attention(cfg["q"][:5], cfg["pool"], solo_idx, np.array([400]),
+                                              small[None, :], cfg["sm_scale"])
+    compare(out[:5], lse[:5], solo_out, solo_lse)
+    compare(out, lse, ref_out, ref_lse)
 
 
 def test_q_zero_lse_is_log_count():
