@@ -267,8 +267,10 @@ __device__ int wg_exclusive_scan(int v, int* s_tmp, int& total) {
 //     one are poisoned (their index segments can no longer be located) and get no keys;
 //   * key_off_b = exclusive scan of (E_b + T), where E_b = ceil(P_b / page) is the number
 //     of prefix entries of the index segment (E_b = P_b when pages are single tokens);
-//   * split length S: fixed, or the smallest multiple of 32 spreading the batch's prefix
-//     tokens over target_units units, at least min_split;
+//   * split length S: fixed, or the smallest multiple of 32 (at least min_split) whose
+//     unit count stays within target_units (one workgroup per CU per M tile): first the
+//     even spread of the batch's prefix tokens, then, if ragged requests round up past
+//     the target, a search upward from there;
 //   * units_b = max(1, ceil(P_b / S)), first_unit_b = exclusive scan of units_b.
 // Fills s_unit[] for unit g (request, key offset, P, first unit, units, error bits) and
 // returns the number of units.  The publishing workgroup also writes the plan out.
@@ -312,21 +314,44 @@ __device__ int plan_units(const PartialArgs& a, int g, bool publish, int* s_tmp,
   }
   int total_keys;
   int key_off = wg_exclusive_scan(segsum, s_tmp, total_keys);
+  auto units_at = [&](int s, int* units) {  // this thread's units at split length s
+    int us = 0;
+#pragma unroll
+    for (int j = 0; j < kPer; j++) {
+      units[j] = (kPer * tid + j < B) ? max(1, (pv[j] + s - 1) / s) : 0;
+      us += units[j];
+    }
+    return us;
+  };
+  auto round_tile = [](int x) { return (x + kTileKeys - 1) / kTileKeys * kTileKeys; };
   int S = a.split_fixed;
-  if (S <= 0) {
+  int units[kPer], total_units;
+  int first = 0;
+  if (S > 0) {
+    first = wg_exclusive_scan(units_at(S, units), s_tmp, total_units);
+  } else {
     int total_prefix = total_keys - B * T;  // prefix tokens (entries are tokens without pages)
     if (a.page_log2 > 0) (void)wg_exclusive_scan(toksum, s_tmp, total_prefix);
-    const int per = (total_prefix + a.target_units - 1) / a.target_units;
-    S = max(a.min_split, (per + kTileKeys - 1) / kTileKeys * kTileKeys);
+    const int U = a.target_units;
+    S = max(a.min_split, round_tile((total_prefix + U - 1) / U));
+    first = wg_exclusive_scan(units_at(S, units), s_tmp, total_units);
+    if (total_units > U && B < U) {
+      // Ragged prefixes round up to more than U units, which would leave some workgroups
+      // for a second round on the CUs.  Sum_b max(1, ceil(P_b / s)) <= total_prefix / s + B,
+      // so s = ceil(total_prefix / (U - B)) fits; search the smallest fitting multiple of
+      // 32 between the two (the unit count does not grow with s).
+      int lo = S + kTileKeys;
+      int hi = max(lo, max(a.min_split, round_tile((total_prefix + (U - B) - 1) / (U - B))));
+      while (lo < hi) {  // lo - 32 does not fit, hi fits; uniform over the workgroup
+        const int mid = (lo + hi) / 2 / kTileKeys * kTileKeys;
+        int tot;
+        (void)wg_exclusive_scan(units_at(mid, units), s_tmp, tot);
+        if (tot <= U) hi = mid; else lo = mid + kTileKeys;
+      }
+      S = hi;
+      first = wg_exclusive_scan(units_at(S, units), s_tmp, total_units);
+    }
   }
-  int units[kPer], usum = 0;
-#pragma unroll
-  for (int j = 0; j < kPer; j++) {
-    units[j] = (kPer * tid + j < B) ? max(1, (pv[j] + S - 1) / S) : 0;
-    usum += units[j];
-  }
-  int total_units;
-  int first = wg_exclusive_scan(usum, s_tmp, total_units);
 #pragma unroll
   for (int j = 0; j < kPer; j++) {
     const int i = kPer * tid + j;

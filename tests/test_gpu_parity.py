@@ -76,6 +76,9 @@ SMALL = [
     (18, [2000], 256, 8, "random", 0),
     (19, [0, 513], 200, 2, "chain", 0),
     (20, [129], 256, 1, "forest", 64),
+    # ragged prefixes that round up past one workgroup per CU: the split search
+    (21, [30000] + [200] * 40, 2, 8, "random", 0),
+    (22, [9000, 130, 4000, 131, 700, 129] * 4, 32, 16, "random", 0),
 ]
 
 
@@ -98,6 +101,20 @@ def test_small_parity(seed, prefix, t, h, tree, split):
     assert plan["total_units"] == first
     if split:
         assert plan["split_len"] == split
+    else:
+        check_auto_split(prefix, plan["split_len"], plan["n_mtiles"])
+
+
+def check_auto_split(prefix, s, n_mtiles):
+    """The automatic split length is the smallest multiple of 32 (at least 128) that keeps
+    the unit count within one workgroup per CU per M tile (256 CUs), when the batch allows."""
+    target = -(-256 // n_mtiles)
+    units = lambda x: sum(max(1, -(-p // x)) for p in prefix)
+    floor = max(128, -(-(-(-sum(prefix) // target)) // 32) * 32)
+    assert s % 32 == 0 and s >= floor
+    if len(prefix) < target:
+        assert units(s) <= target
+        assert s == floor or units(s - 32) > target
 
 
 # --------------------------------------------------------------------------- workload configs
@@ -113,7 +130,9 @@ def test_config_parity_full(i):
 @pytest.mark.parametrize("i", [3, 4])
 def test_config_parity_sampled(i):
     cfg = synth.make_config(i)
-    out, lse, _ = run_gpu(cfg)
+    out, lse, v = run_gpu(cfg)
+    plan = v.read_plan()
+    check_auto_split(cfg["prefix_lens"].tolist(), plan["split_len"], plan["n_mtiles"])
     rng = np.random.default_rng(100 + i)
     t = cfg["tree_nodes"]
     nodes = [(b, n) for b in range(cfg["batch"]) for n in sorted({0, t - 1, *rng.integers(0, t, 6).tolist()})]
