@@ -41,14 +41,14 @@ typedef __attribute__((address_space(3))) void lds_void;
 // distance 2^r, so ceil(log2 T) rounds suffice whatever the depth.  Thread i < T owns node
 // i (the workgroup has at least T threads); s_m holds T x W words, s_jump T ints.  Parents
 // must satisfy -1 <= parent[i] < i; the result says whether one does not (then the masks
-// are not meaningful).  Called by every thread of the workgroup.
+// are not meaningful).  Called by every thread of the workgroup; thread i < T passes
+// parent[i] in p.
 template <int W>
-__device__ bool build_masks(const int32_t* __restrict__ par, int T, uint64_t* s_m, int* s_jump) {
+__device__ bool build_masks(int p, int T, uint64_t* s_m, int* s_jump) {
   const int i = threadIdx.x;
   int jmp = -1;
   bool bad = false;
   if (i < T) {
-    const int p = par[i];
     bad = p < -1 || p >= i;
     jmp = bad ? -1 : p;
 #pragma unroll
@@ -84,7 +84,7 @@ __global__ __launch_bounds__(kThreads) void k_tree_masks(const int32_t* __restri
   __shared__ uint64_t s_m[kMaxTree * kMaxTreeWords];
   __shared__ int s_jump[kMaxTree];
   const int b = blockIdx.x, i = threadIdx.x;
-  const bool bad = build_masks<kMaxTreeWords>(par + (size_t)b * T, T, s_m, s_jump);
+  const bool bad = build_masks<kMaxTreeWords>(i < T ? par[(size_t)b * T + i] : 0, T, s_m, s_jump);
   const int W = (T + 63) >> 6;
   for (int k = i; k < T * W; k += kThreads) {
     const int node = k / W, w = k - node * W;
@@ -288,16 +288,14 @@ __device__ int plan_units(const PartialArgs& a, int g, bool publish, int* s_tmp,
   constexpr int kPer = kMaxBatch / kThreads;  // requests per thread
   int pv[kPer], bad[kPer];
   int nbad = 0;
+  // all of a thread's loads go out before the first wait (addresses clamped into the batch)
+#pragma unroll
+  for (int j = 0; j < kPer; j++) pv[j] = a.prefix_lens[min(kPer * tid + j, B - 1)];
 #pragma unroll
   for (int j = 0; j < kPer; j++) {
     const int i = kPer * tid + j;
-    pv[j] = 0;
-    bad[j] = 0;
-    if (i < B) {
-      const int P = a.prefix_lens[i];
-      bad[j] = (P < 0 || P > a.max_prefix) ? 1 : 0;
-      pv[j] = P;
-    }
+    bad[j] = (i < B && (pv[j] < 0 || pv[j] > a.max_prefix)) ? 1 : 0;
+    if (i >= B) pv[j] = 0;
     nbad += bad[j];
   }
   int tot_bad;
@@ -445,59 +443,14 @@ void k_partial(PartialArgs a) {
   // iteration, and each row copies its own mask into registers before that.
   constexpr int kW = kBigTree ? kMaxTreeWords : 1;
   uint64_t* s_m = reinterpret_cast<uint64_t*>(smem + 2 * kTileBytes);
-  if (last) {
-    int* s_jump = reinterpret_cast<int*>(smem + 2 * kTileBytes + kMaxTree * kMaxTreeWords * 8);
-    if (build_masks<kW>(a.tree_parent + (size_t)b * a.T, a.T, s_m, s_jump)) {
-      req_err |= kErrBadParent;
-      if (tid == 0 && mt == 0) atomicOr(a.sticky_err, kErrBadParent);
-    }
-  }
-
   const int r = mt * kRowsPerBlock + w * kRowsPerWave + lrow;
   const bool rvalid = r < a.M;
-  if (req_err) {  // poisoned request: NaN partials, which the merge turns into NaN rows
-    if (rvalid && h == 0) a.part_lse[(size_t)g * a.M + r] = __uint_as_float(0x7FC00000u);
-    return;
-  }
-
-  // Contiguous-run fast path (row a.5): if the unit's prefix slots are one run first,
-  // first+1, ..., rows are addressed from `first` without reading the index table again.
-  auto slot_at = [&](int k) -> int {  // slot of the unit's prefix key k
-    return kPaged ? page_slot(pidx[(kbeg + k) >> a.page_log2], kbeg + k) : pidx[k];
-  };
-  int run_base = -1;
-  if (!(a.flags & 1u) && npk > 0) {
-    const int first = slot_at(0);
-    int ok = first >= 0 && (int64_t)first + npk <= a.pool_slots;
-    for (int k0 = 0; ok && k0 < npk; k0 += kThreads) {
-      const int k = k0 + tid;
-      ok = __syncthreads_and(k >= npk || slot_at(k) == first + k);
-    }
-    if (ok) run_base = first;
-  }
-
-  // B operand of the score MFMA: Q[row][16kk + 8h .. +7] (bf16 pairs).  Row r of the request
-  // is (node r / H, head r % H).  The first kQReg k-steps stay in VGPRs for the whole unit;
-  // the rest are parked in this wave's LDS slice (lane-major, conflict-free).
-  typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
-  lds_u32x4* qlds = (lds_u32x4*)(lds + kTileBufs * kTileBytes + w * kQLdsBytes) + lane;
-  u32x4 qf[kQReg];
-  {
-    // rows past M (last M tile) read the request's last row; their results are dropped
-    const u32x4* qp = reinterpret_cast<const u32x4*>(a.q + ((size_t)b * a.M + (rvalid ? r : a.M - 1)) * kLatent) + h;
-#pragma unroll
-    for (int kk = 0; kk < kQReg; kk++) qf[kk] = qp[2 * kk];
-#pragma unroll
-    for (int kk = kQReg; kk < 36; kk++) qlds[(kk - kQReg) * 64] = qp[2 * kk];
-  }
-  uint64_t anc[kW];
-#pragma unroll
-  for (int w = 0; w < kW; w++) anc[w] = (last && rvalid) ? s_m[(r / a.H) * kW + w] : ~0ull;
 
   // Gather geometry: thread tid loads 9 chunks of key kt of every tile.
   const int kt = tid >> 3;
   const int kxor = (tid & 7) ^ swz(kt);
   int bad_index = 0;
+  int run_base = -1;  // first slot of the unit's prefix run, if it is one (decided below)
 
   // Pool slot of this thread's key of tile t (tail keys re-read the tile's first key), in two
   // steps: load_index issues the table load, slot_of turns its value into the slot once it is
@@ -516,7 +469,6 @@ void k_partial(PartialArgs a) {
     if (kPaged && t < npt) return page_slot(loaded, kbeg + t * kTileKeys + key_of(t));
     return loaded;
   };
-  auto fetch_index = [&](int t) -> int { return slot_of(t, load_index(t)); };
   // Source row of this thread's key and the wave's LDS target.  A slot outside the pool is
   // never read: row 0 stands in and the error is recorded when the unit ends.
   auto tile_src = [&](int idx) -> const char* {
@@ -545,6 +497,72 @@ void k_partial(PartialArgs a) {
 #pragma unroll
     for (int j = 0; j < 9; j++) issue_piece(src, dst, j);
   };
+
+  // Contiguous-run fast path (row a.5): if the unit's prefix slots are one run first,
+  // first+1, ..., rows are addressed from `first` without reading the index table again.
+  auto slot_at = [&](int k) -> int {  // slot of the unit's prefix key k
+    return kPaged ? page_slot(pidx[(kbeg + k) >> a.page_log2], kbeg + k) : pidx[k];
+  };
+
+  // Reads that depend only on the plan go out together: the run check's first keys, the
+  // index entries of tiles 0..2 and the tree parents.  Q follows the first gathers (loads
+  // complete in issue order, and the compiler's waits before the gathers cover every load
+  // issued so far), so its latency overlaps theirs.  A poisoned request's segment offsets
+  // are unknown, so nothing is read from its index segment.
+  const bool plan_ok = req_err == 0;
+  const bool check_run = plan_ok && !(a.flags & 1u) && npk > 0;
+  int run_first = 0, run_mine = 0;
+  if (check_run) {
+    run_first = slot_at(0);
+    if (tid < npk) run_mine = slot_at(tid);
+  }
+  int raw0 = 0, raw1 = 0, raw2 = 0;  // index-table entries of tiles 0..2 (this thread's key)
+  if (plan_ok) {
+    raw0 = load_index(0);
+    if (ntiles > 1) raw1 = load_index(1);
+    if (ntiles > 2) raw2 = load_index(2);
+  }
+  int par_i = 0;
+  if (last && tid < a.T) par_i = a.tree_parent[(size_t)b * a.T + tid];
+  int* s_jump = reinterpret_cast<int*>(smem + 2 * kTileBytes + kMaxTree * kMaxTreeWords * 8);
+  auto masks = [&]() {
+    if (build_masks<kW>(par_i, a.T, s_m, s_jump)) {
+      req_err |= kErrBadParent;
+      if (tid == 0 && mt == 0) atomicOr(a.sticky_err, kErrBadParent);
+    }
+  };
+  auto poison = [&]() {  // poisoned request: NaN partials, which the merge turns into NaN rows
+    if (rvalid && h == 0) a.part_lse[(size_t)g * a.M + r] = __uint_as_float(0x7FC00000u);
+  };
+  if (!plan_ok) {
+    if (last) masks();  // its parents are still checked and reported
+    poison();
+    return;
+  }
+
+  if (check_run) {
+    int ok = run_first >= 0 && (int64_t)run_first + npk <= a.pool_slots;  // uniform
+    ok = __syncthreads_and(ok && (tid >= npk || run_mine == run_first + tid));
+    // longer units: kRunBatch further keys per thread in flight per round
+    constexpr int kRunBatch = 8;
+    for (int k0 = kThreads; ok && k0 < npk; k0 += kThreads * kRunBatch) {
+      int v[kRunBatch];
+#pragma unroll
+      for (int j = 0; j < kRunBatch; j++) {
+        const int k = k0 + j * kThreads + tid;
+        v[j] = k < npk ? slot_at(k) : run_first + k;
+      }
+      bool mine = true;
+#pragma unroll
+      for (int j = 0; j < kRunBatch; j++) mine = mine && v[j] == run_first + k0 + j * kThreads + tid;
+      ok = __syncthreads_and(mine);
+    }
+    if (ok) run_base = run_first;
+  }
+  uint64_t anc[kW];  // this row's ancestor-mask words (filled before the first scores)
+  u32x4 qf[kQReg];   // Q k-steps kept in VGPRs (filled after the first gathers)
+  typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+  lds_u32x4* qlds = (lds_u32x4*)(lds + kTileBufs * kTileBytes + w * kQLdsBytes) + lane;
 
   // Per-lane LDS offsets.  K operand of the score MFMA: key lrow, chunk 2kk + h.
   int koff[4];
@@ -701,20 +719,25 @@ void k_partial(PartialArgs a) {
   f32x16 sacc;       // S^T of tile t
   Soft dummy_soft;
   const f32x16 zero16 = {};
-  auto start_pass = [&]() {
+  // First half of a pass: the gathers of tiles 0 and 1.  The index entries of tiles 0..2
+  // were loaded before (the first pass: in the prologue; a restart: just before), and all
+  // three have landed before any gather goes out, since the compiler cannot see a gather's
+  // completion and a wait for an index issued after one would also wait for it.
+  auto start_gathers = [&](int e0, int e1, int e2) {
     t = 0;
     bi = 0;
-    // the three index loads go out together, before any gather (whose completion the
-    // compiler cannot see, so a wait for an index issued after one would also wait for it)
-    const int i0 = fetch_index(0);
-    const int i1 = ntiles > 1 ? fetch_index(1) : 0;
-    idx_next = ntiles > 2 ? load_index(2) : 0;
+    const int i0 = slot_of(0, e0);
+    const int i1 = ntiles > 1 ? slot_of(1, e1) : 0;
+    idx_next = e2;
     const char* src0 = tile_src(i0);
     const char* src1 = tile_src(i1);
     const int i2 = idx_next;
     asm volatile("" ::"v"(i2));  // idx_next has landed too
     issue_tile(0, src0);
     if (ntiles > 1) issue_tile(1, src1);
+  };
+  // Second half: once tile 0 has landed everywhere, its scores.
+  auto start_scores = [&]() {
     if (ntiles > 1) {
       __builtin_amdgcn_s_waitcnt(0x0F79);  // vmcnt(9): tile 0 landed (tile 1 may not)
     } else {
@@ -725,7 +748,30 @@ void k_partial(PartialArgs a) {
     sacc = s_chain(IntC<-1>{}, IntC<0>{}, lds, nullptr, 0u, zero16, 0.f, dummy_soft, s_pre(lds));
   };
   MLV_ZERO_O();  // O^T[d = 32db + ..][row] accumulates in a[0..255]
-  start_pass();
+  start_gathers(raw0, raw1, raw2);
+  // B operand of the score MFMA: Q[row][16kk + 8h .. +7] (bf16 pairs).  Row r of the request
+  // is (node r / H, head r % H).  The first kQReg k-steps stay in VGPRs for the whole unit;
+  // the rest are parked in this wave's LDS slice (lane-major, conflict-free).
+  {
+    u32x4 qt[36 - kQReg];
+    // rows past M (last M tile) read the request's last row; their results are dropped
+    const u32x4* qp = reinterpret_cast<const u32x4*>(a.q + ((size_t)b * a.M + (rvalid ? r : a.M - 1)) * kLatent) + h;
+#pragma unroll
+    for (int kk = 0; kk < kQReg; kk++) qf[kk] = qp[2 * kk];
+#pragma unroll
+    for (int kk = kQReg; kk < 36; kk++) qt[kk - kQReg] = qp[2 * kk];
+    if (last) masks();
+    if (req_err) {  // a bad parent: the tiles' gathers must land before the workgroup ends
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      poison();
+      return;
+    }
+#pragma unroll
+    for (int kk = kQReg; kk < 36; kk++) qlds[(kk - kQReg) * 64] = qt[kk - kQReg];
+  }
+#pragma unroll
+  for (int w = 0; w < kW; w++) anc[w] = (last && rvalid) ? s_m[(r / a.H) * kW + w] : ~0ull;
+  start_scores();
   for (;;) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's loads of tile t+1 landed
     __syncthreads();                     // ... and everyone's; PV(t-1) finished everywhere
@@ -751,7 +797,11 @@ void k_partial(PartialArgs a) {
       asm volatile("s_nop 15\n\ts_nop 3" ::: "memory");  // PV MFMAs of the last tile have landed
       MLV_ZERO_O();
       lrun = 0.f;
-      start_pass();
+      {
+        const int e0 = load_index(0), e1 = ntiles > 1 ? load_index(1) : 0, e2 = ntiles > 2 ? load_index(2) : 0;
+        start_gathers(e0, e1, e2);
+        start_scores();
+      }
       continue;
     }
 
