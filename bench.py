@@ -315,6 +315,8 @@ def main() -> int:
     ap.add_argument("--config", type=int, default=3, help="workload index (workloads.synth.CONFIGS)")
     ap.add_argument("--variant", default=None, help="workload variant, e.g. contiguous or sorted")
     ap.add_argument("--warm", action="store_true", help="do not flush caches between calls")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of the call captured in a HIP graph (the flush stays outside it)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--split", type=int, default=0, help="fixed split length (0 = automatic)")
@@ -371,6 +373,20 @@ def main() -> int:
             flush.add_(1.0)
         step()
     torch.cuda.synchronize()
+    call = step
+    if args.graph:  # the same call, captured once on a side stream and replayed on this one
+        gs = torch.cuda.Stream(device=dev)
+        gs.wait_stream(stream)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=gs):
+            v.run(q, pool, kv_idx, plens, par, out=out, lse=lse, stream=gs)
+        torch.cuda.synchronize()
+        call = graph.replay
+        for _ in range(args.warmup):
+            if not args.warm:
+                flush.add_(1.0)
+            call()
+        torch.cuda.synchronize()
 
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
@@ -382,7 +398,7 @@ def main() -> int:
         if not args.warm:
             flush.add_(1.0)
         starts[k].record(stream)
-        step()
+        call()
         ends[k].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -436,7 +452,8 @@ def main() -> int:
         "config": {"workload": workload,
                    "batch": b, "tree_nodes": t, "heads": h,
                    "prefix_lens": [int(x) for x in cfg["prefix_lens"]], "pool_slots": cfg["slots"],
-                   "split": args.split or "auto", "cache": "warm" if args.warm else "flushed 1 GiB before each call"},
+                   "split": args.split or "auto", "cache": "warm" if args.warm else "flushed 1 GiB before each call",
+                   "call": "HIP graph replay" if args.graph else "eager"},
         "us_per_call": {"median": round(med_ms * 1e3, 2), "p10": round(float(p10) * 1e3, 2),
                         "p90": round(float(p90) * 1e3, 2)},
         "pct_hbm_peak": round(100 * kv_gbs / HBM_PEAK_GBS, 2),
