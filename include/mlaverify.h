@@ -53,7 +53,8 @@ extern "C" {
 
 /* Status codes. */
 #define MLAVERIFY_OK 0
-#define MLAVERIFY_ERR_INVALID_ARG (-1)    /* null pointer, misalignment, size out of range */
+#define MLAVERIFY_ERR_INVALID_ARG (-1)    /* null pointer, misalignment, size out of range, or a call on a
+                                             handle whose device is not the current one */
 #define MLAVERIFY_ERR_UNSUPPORTED (-2)    /* a configuration the kernels do not implement */
 #define MLAVERIFY_ERR_NO_MEMORY (-3)      /* library-owned workspace allocation failed */
 #define MLAVERIFY_ERR_WORKSPACE (-4)      /* caller workspace smaller than mlaverify_workspace_bytes */

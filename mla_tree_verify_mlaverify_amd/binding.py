@@ -222,9 +222,10 @@ class Verifier:
             lse = torch.empty((b * t, h), dtype=torch.float32, device=dev)
         _check(out, "out", torch.bfloat16, (b * t, h, V_DIM), dev)
         _check(lse, "lse", torch.float32, (b * t, h), dev)
-        rc = self.lib.mlaverify_run(self.handle, b, t, q.data_ptr(), kv_pool.data_ptr(), kv_indices.data_ptr(),
-                                    prefix_lens.data_ptr(), tree_parent.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                                    _stream_handle(stream))
+        with torch.cuda.device(dev):  # the library launches on its handle's device only
+            rc = self.lib.mlaverify_run(self.handle, b, t, q.data_ptr(), kv_pool.data_ptr(), kv_indices.data_ptr(),
+                                        prefix_lens.data_ptr(), tree_parent.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                        _stream_handle(stream))
         if rc != OK:
             raise MlaVerifyError(rc, "mlaverify_run")
         self.last_batch = b
@@ -243,8 +244,9 @@ class Verifier:
         if kv_indices.dim() != 1:
             raise ValueError("kv_indices must be 1-D")
         _check(kv_pool, "kv_pool", torch.bfloat16, (self.cfg.pool_slots, self.cfg.kv_row_stride), dev)
-        rc = self.lib.mlaverify_relocate(self.handle, b, tree_nodes, kv_pool.data_ptr(), kv_indices.data_ptr(),
-                                         prefix_lens.data_ptr(), dst_start.data_ptr(), _stream_handle(stream))
+        with torch.cuda.device(dev):  # the library launches on its handle's device only
+            rc = self.lib.mlaverify_relocate(self.handle, b, tree_nodes, kv_pool.data_ptr(), kv_indices.data_ptr(),
+                                             prefix_lens.data_ptr(), dst_start.data_ptr(), _stream_handle(stream))
         if rc != OK:
             raise MlaVerifyError(rc, "mlaverify_relocate")
 
@@ -263,9 +265,10 @@ class Verifier:
         accept_len = torch.empty(b, dtype=torch.int32, device=dev)
         accepted = torch.empty((b, t), dtype=torch.int32, device=dev)
         bonus = torch.empty(b, dtype=torch.int32, device=dev)
-        rc = self.lib.mlaverify_accept(self.handle, b, t, logits.shape[2], logits.data_ptr(), draft_tokens.data_ptr(),
-                                       tree_parent.data_ptr(), accept_len.data_ptr(), accepted.data_ptr(),
-                                       bonus.data_ptr(), _stream_handle(stream))
+        with torch.cuda.device(dev):  # the library launches on its handle's device only
+            rc = self.lib.mlaverify_accept(self.handle, b, t, logits.shape[2], logits.data_ptr(), draft_tokens.data_ptr(),
+                                           tree_parent.data_ptr(), accept_len.data_ptr(), accepted.data_ptr(),
+                                           bonus.data_ptr(), _stream_handle(stream))
         if rc != OK:
             raise MlaVerifyError(rc, "mlaverify_accept")
         return accept_len, accepted, bonus

@@ -93,6 +93,12 @@ void release_profile(mlaverify_handle* hd) {
 }
 }  // namespace
 
+// Launches go to the handle's device only: its workspace lives there.
+static bool on_handle_device(const mlaverify_handle* hd) {
+  int dev = -1;
+  return hipGetDevice(&dev) == hipSuccess && dev == hd->device;
+}
+
 extern "C" {
 
 int mlaverify_validate_config(const mlaverify_config* c) {
@@ -169,6 +175,7 @@ int mlaverify_run(mlaverify_t hd, int32_t batch, int32_t T, const void* q, const
                   const int32_t* kv_indices, const int32_t* prefix_lens, const int32_t* tree_parent, void* out,
                   float* lse, void* stream) {
   if (!hd) return MLAVERIFY_ERR_INVALID_ARG;
+  if (!on_handle_device(hd)) return MLAVERIFY_ERR_INVALID_ARG;
   const mlaverify_config& c = hd->cfg;
   if (batch < 1 || batch > c.max_batch || T < 1 || T > c.max_tree_nodes) return MLAVERIFY_ERR_INVALID_ARG;
   if (!q || !kv_pool || !kv_indices || !prefix_lens || !tree_parent || !out || !lse) return MLAVERIFY_ERR_INVALID_ARG;
@@ -234,6 +241,7 @@ int mlaverify_run(mlaverify_t hd, int32_t batch, int32_t T, const void* q, const
 int mlaverify_relocate(mlaverify_t hd, int32_t batch, int32_t T, void* kv_pool, int32_t* kv_indices,
                        const int32_t* prefix_lens, const int32_t* dst_start, void* stream) {
   if (!hd) return MLAVERIFY_ERR_INVALID_ARG;
+  if (!on_handle_device(hd)) return MLAVERIFY_ERR_INVALID_ARG;
   const mlaverify_config& c = hd->cfg;
   if (batch < 1 || batch > c.max_batch || T < 1 || T > c.max_tree_nodes) return MLAVERIFY_ERR_INVALID_ARG;
   if (!kv_pool || !kv_indices || !prefix_lens || !dst_start) return MLAVERIFY_ERR_INVALID_ARG;
@@ -265,6 +273,7 @@ int mlaverify_accept(mlaverify_t hd, int32_t batch, int32_t T, int32_t vocab, co
                      const int32_t* draft_tokens, const int32_t* tree_parent, int32_t* accept_len, int32_t* accepted,
                      int32_t* bonus, void* stream) {
   if (!hd) return MLAVERIFY_ERR_INVALID_ARG;
+  if (!on_handle_device(hd)) return MLAVERIFY_ERR_INVALID_ARG;
   const mlaverify_config& c = hd->cfg;
   if (batch < 1 || batch > c.max_batch || T < 1 || T > c.max_tree_nodes || vocab < 1) return MLAVERIFY_ERR_INVALID_ARG;
   if (!logits || !draft_tokens || !tree_parent || !accept_len || !accepted || !bonus) return MLAVERIFY_ERR_INVALID_ARG;
