@@ -1,0 +1,71 @@
+"""Host logic of bench.py, pinned on the CPU: the algorithmic bytes and flops behind every
+reported rate and roofline fraction, the tie between stored profiler counters and the
+kernel sources, and the single-GPU guard."""
+
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+import bench
+from workloads import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def visible_counts(parents, prefix):
+    """Keys each node sees, by walking its ancestor chain (the node itself included)."""
+    out = []
+    for i in range(len(parents)):
+        n, j = 0, i
+        while j >= 0:
+            n += 1
+            j = parents[j]
+        out.append(prefix + n)
+    return out
+
+
+def test_tiny_counts_by_hand():
+    # 1 request, 256-token prefix, tree [-1,0,1,2,0,4,1,6]: visible keys 257..260 per node
+    cfg = synth.make_config(0)
+    c = bench.algorithmic_counts(cfg)
+    assert visible_counts(list(cfg["tree_parent"][0]), 256) == [257, 258, 259, 260, 258, 259, 259, 260]
+    assert c["keys"] == 264
+    assert c["kv_bytes"] == 264 * 1152
+    assert c["flops"] == 2 * 8 * 2070 * 1088  # 2 flops x heads x visible keys x (576 + 512)
+    assert c["total_bytes"] == 264 * 1152 + 264 * 4 + 8 * 8 * 576 * 2 + 8 * 8 * (512 * 2 + 4)
+
+
+def test_counts_match_ancestor_walk_on_random_batches():
+    rng = np.random.default_rng(11)
+    for _ in range(5):
+        b, t, h = int(rng.integers(1, 5)), int(rng.integers(1, 40)), int(rng.integers(1, 17))
+        prefix = [int(x) for x in rng.integers(0, 3000, b)]
+        cfg = synth.small_config(int(rng.integers(0, 1 << 30)), batch=b, prefix=prefix, tree_nodes=t, heads=h,
+                                 slots=2 * (sum(prefix) + b * t) + 8)
+        c = bench.algorithmic_counts(cfg)
+        vis = sum(sum(visible_counts(list(cfg["tree_parent"][k]), prefix[k])) for k in range(b))
+        assert c["flops"] == 2 * h * vis * 1088
+        assert c["keys"] == sum(prefix) + b * t
+        assert c["prefix_flops"] == 2 * h * t * sum(prefix) * 1088
+
+
+def test_stored_traffic_follows_the_kernel_sources():
+    # the committed counters are reported only for the sources they were taken from
+    path = os.path.join(ROOT, "profiles", "k_partial_p185000_t64_h8.md")
+    text = open(path).read()
+    recorded = text.split('"source_sha256_16": "')[1].split('"')[0]
+    got = bench.stored_traffic("p185000_t64_h8")
+    if recorded == bench.source_hash():
+        assert got is not None and got > 213_000_000  # at least the KV rows of one launch
+    else:
+        assert got is None
+    assert bench.stored_traffic("no_such_workload") is None
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
