@@ -282,7 +282,7 @@ struct UnitPlan {
 // Entries of a prefix of p tokens in its index segment: one per page of 2^page_log2 slots.
 __device__ __forceinline__ int seg_entries(int p, int page_log2) { return (p + (1 << page_log2) - 1) >> page_log2; }
 
-__device__ int plan_units(const PartialArgs& a, int g, bool publish, int* s_tmp, int* s_unit) {
+__device__ int plan_units(const PartialArgs& a, int g, bool publish, int* s_tmp, int* s_unit, int* s_scr) {
   const int tid = threadIdx.x;
   const int B = a.batch, T = a.T;
   constexpr int kPer = kMaxBatch / kThreads;  // requests per thread
@@ -340,11 +340,45 @@ __device__ int plan_units(const PartialArgs& a, int g, bool publish, int* s_tmp,
       // 32 between the two (the unit count does not grow with s).
       int lo = S + kTileKeys;
       int hi = max(lo, max(a.min_split, round_tile((total_prefix + (U - B) - 1) / (U - B))));
-      while (lo < hi) {  // lo - 32 does not fit, hi fits; uniform over the workgroup
-        const int mid = (lo + hi) / 2 / kTileKeys * kTileKeys;
-        int tot;
-        (void)wg_exclusive_scan(units_at(mid, units), s_tmp, tot);
-        if (tot <= U) hi = mid; else lo = mid + kTileKeys;
+      // Invariant of both searches: lo - 32 does not fit, hi fits; uniform over the workgroup.
+      if (B <= kFewRequests) {
+        // Few requests: every thread counts the units of its own candidate length, so one
+        // round tests up to kThreads lengths (spaced st apart) at once.
+#pragma unroll
+        for (int j = 0; j < kPer; j++)
+          if (kPer * tid + j < B) s_scr[kPer * tid + j] = pv[j];
+        __syncthreads();
+        while (lo < hi) {
+          const int n = (hi - lo) / kTileKeys;  // lengths lo, lo + 32, ..., hi - 32 are open
+          const int st = kTileKeys * ((n + kThreads - 1) / kThreads);
+          const int m = (hi - lo + st - 1) / st;  // candidates lo + t st, t < m, all below hi
+          const int c = lo + tid * st;
+          bool fits = false;
+          if (tid < m) {
+            int us = 0;
+            for (int k = 0; k < B; k++) us += max(1, (s_scr[k] + c - 1) / c);
+            fits = us <= U;
+          }
+          if (tid == 0) s_tmp[0] = kThreads;
+          __syncthreads();
+          if (fits) atomicMin(&s_tmp[0], tid);
+          __syncthreads();
+          const int t0 = s_tmp[0];
+          __syncthreads();
+          if (t0 < m) {  // the smallest fitting candidate; the one before it does not fit
+            hi = lo + t0 * st;
+            lo = t0 == 0 ? hi : hi - st + kTileKeys;
+          } else {
+            lo = lo + (m - 1) * st + kTileKeys;
+          }
+        }
+      } else {
+        while (lo < hi) {
+          const int mid = (lo + hi) / 2 / kTileKeys * kTileKeys;
+          int tot;
+          (void)wg_exclusive_scan(units_at(mid, units), s_tmp, tot);
+          if (tot <= U) hi = mid; else lo = mid + kTileKeys;
+        }
       }
       S = hi;
       first = wg_exclusive_scan(units_at(S, units), s_tmp, total_units);
@@ -412,7 +446,8 @@ void k_partial(PartialArgs a) {
   const int slot = bid >> 3;
   const int mt = slot % a.n_mtiles;
   const int g = (slot / a.n_mtiles) * 8 + (bid & 7);
-  const int total_units = plan_units(a, g, g == 0 && mt == 0, s_tmp, s_unit);
+  // (tile buffer 0 is the plan's scratch: no gather writes it before the plan is done)
+  const int total_units = plan_units(a, g, g == 0 && mt == 0, s_tmp, s_unit, reinterpret_cast<int*>(smem));
   if (g >= total_units || g >= a.units_cap) return;
   const int b = s_unit[0];
   const int key_off = s_unit[1];

@@ -29,6 +29,7 @@ constexpr int kMaxPage = 1024;         // largest prefix page (block-table) size
 constexpr int kMaxBatch = 1024;        // one plan thread per request
 constexpr int kTargetBlocks = 256;     // workgroups the split aims for (one per CU on MI355X)
 constexpr int kMinSplit = 128;         // shortest automatic prefix split, in tokens
+constexpr int kFewRequests = 32;       // split search: candidate lengths in parallel up to this batch
 
 // Device-side error bits (mirrors MLAVERIFY_DEVERR_* in the public header).
 constexpr uint32_t kErrBadParent = 0x1u;
