@@ -215,6 +215,7 @@ int mlaverify_run(mlaverify_t hd, int32_t batch, int32_t T, const void* q, const
   ka.flags = c.flags;
   ka.page_log2 = page_log2(c.page_size);
   ka.max_page = (int32_t)((c.pool_slots - 1) >> ka.page_log2);
+  ka.group_xcd = units_grid >= 8 ? 1 : 0;  // too few units to fill 8 XCDs one unit apiece
 
   MergeArgs ma;
   ma.req = ka.req;

@@ -442,10 +442,17 @@ void k_partial(PartialArgs a) {
 
   // Workgroup -> (unit, M tile).  Consecutive workgroups go to consecutive XCDs, so the M
   // tiles of one unit are given ids that are equal mod 8: they share an XCD and its L2.
+  // With fewer than 8 units that would leave XCDs idle; the M tiles then go round-robin.
   const int bid = blockIdx.x;
-  const int slot = bid >> 3;
-  const int mt = slot % a.n_mtiles;
-  const int g = (slot / a.n_mtiles) * 8 + (bid & 7);
+  int mt, g;
+  if (a.group_xcd) {
+    const int slot = bid >> 3;
+    mt = slot % a.n_mtiles;
+    g = (slot / a.n_mtiles) * 8 + (bid & 7);
+  } else {
+    mt = bid % a.n_mtiles;
+    g = bid / a.n_mtiles;
+  }
   // (tile buffer 0 is the plan's scratch: no gather writes it before the plan is done)
   const int total_units = plan_units(a, g, g == 0 && mt == 0, s_tmp, s_unit, reinterpret_cast<int*>(smem));
   if (g >= total_units || g >= a.units_cap) return;

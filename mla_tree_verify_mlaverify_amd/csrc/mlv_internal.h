@@ -76,6 +76,7 @@ struct PartialArgs {
   uint32_t flags;
   int32_t page_log2;     // prefix pages of 2^page_log2 slots (0: one slot per token)
   int32_t max_page;      // largest valid page id, (pool_slots - 1) >> page_log2
+  int32_t group_xcd;     // 1: the M tiles of a unit share an XCD; 0: M tiles round-robin
 };
 
 struct MergeArgs {

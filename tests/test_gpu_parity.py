@@ -140,6 +140,19 @@ def test_config_parity_sampled(i):
     print(i, compare(out, lse, ref_out, ref_lse))
 
 
+def test_largest_rows_per_request():
+    # 128 heads x 256 nodes = 32,768 rows per request: 256 M tiles, one unit each, four mask
+    # words per row; the oracle evaluates a sample of the nodes.
+    cfg = synth.small_config(31, batch=1, prefix=[300], tree_nodes=256, heads=128,
+                             slots=4096, tree="random", q_scale=1.0)
+    out, lse, v = run_gpu(cfg)
+    plan = v.read_plan()
+    assert plan["n_mtiles"] == 256 and plan["total_units"] == 1
+    nodes = [(0, n) for n in (0, 1, 77, 128, 200, 255)]
+    ref_out, ref_lse = run_oracle(cfg, nodes=nodes)
+    compare(out, lse, ref_out, ref_lse)
+
+
 # --------------------------------------------------------------------------- sensitive variants
 
 @pytest.mark.parametrize("variant", ["sorted", "contiguous", "sharp", "needle_prefix", "needle_tree", "prefix0",
