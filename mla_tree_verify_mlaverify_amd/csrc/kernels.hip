@@ -269,9 +269,11 @@ __device__ int wg_exclusive_scan(int v, int* s_tmp, int& total) {
 //     of prefix entries of the index segment (E_b = P_b when pages are single tokens);
 //   * split length S: fixed, or the smallest multiple of 32 (at least min_split) whose
 //     unit count stays within target_units (one workgroup per CU per M tile): first the
-//     even spread of the batch's prefix tokens, then, if ragged requests round up past
-//     the target, a search upward from there;
-//   * units_b = max(1, ceil(P_b / S)), first_unit_b = exclusive scan of units_b.
+//     even spread of the batch's prefix tokens and tree keys, then, if ragged requests
+//     round up past the target, a search upward from there;
+//   * units_b = max(1, ceil(P_b / S)) under a fixed split; under an automatic one the tree
+//     tiles count too, units_b = max(1, min(ceil((P_b + tree keys) / S), ceil(P_b / S) + 1));
+//     first_unit_b = exclusive scan of units_b.
 // Fills s_unit[] for unit g (request, key offset, P, first unit, units, error bits) and
 // returns the number of units.  The publishing workgroup also writes the plan out.
 struct UnitPlan {
@@ -312,17 +314,22 @@ __device__ int plan_units(const PartialArgs& a, int g, bool publish, int* s_tmp,
   }
   int total_keys;
   int key_off = wg_exclusive_scan(segsum, s_tmp, total_keys);
+  auto round_tile = [](int x) { return (x + kTileKeys - 1) / kTileKeys * kTileKeys; };
+  int S = a.split_fixed;
+  // Keys a request's units share: its prefix, plus its tree tiles under an automatic split,
+  // so that the last unit (which also covers the tree) gets a smaller prefix share.  A
+  // unit beyond the prefix units is allowed only as that last one.
+  const int tkeys = S > 0 ? 0 : round_tile(T);
+  auto units_of = [&](int p, int s) { return max(1, min((p + tkeys + s - 1) / s, (p + s - 1) / s + 1)); };
   auto units_at = [&](int s, int* units) {  // this thread's units at split length s
     int us = 0;
 #pragma unroll
     for (int j = 0; j < kPer; j++) {
-      units[j] = (kPer * tid + j < B) ? max(1, (pv[j] + s - 1) / s) : 0;
+      units[j] = (kPer * tid + j < B) ? units_of(pv[j], s) : 0;
       us += units[j];
     }
     return us;
   };
-  auto round_tile = [](int x) { return (x + kTileKeys - 1) / kTileKeys * kTileKeys; };
-  int S = a.split_fixed;
   int units[kPer], total_units;
   int first = 0;
   if (S > 0) {
@@ -331,15 +338,16 @@ __device__ int plan_units(const PartialArgs& a, int g, bool publish, int* s_tmp,
     int total_prefix = total_keys - B * T;  // prefix tokens (entries are tokens without pages)
     if (a.page_log2 > 0) (void)wg_exclusive_scan(toksum, s_tmp, total_prefix);
     const int U = a.target_units;
-    S = max(a.min_split, round_tile((total_prefix + U - 1) / U));
+    const int work = total_prefix + B * tkeys;
+    S = max(a.min_split, round_tile((work + U - 1) / U));
     first = wg_exclusive_scan(units_at(S, units), s_tmp, total_units);
     if (total_units > U && B < U) {
       // Ragged prefixes round up to more than U units, which would leave some workgroups
-      // for a second round on the CUs.  Sum_b max(1, ceil(P_b / s)) <= total_prefix / s + B,
-      // so s = ceil(total_prefix / (U - B)) fits; search the smallest fitting multiple of
-      // 32 between the two (the unit count does not grow with s).
+      // for a second round on the CUs.  Sum_b units_b <= Sum_b max(1, ceil((P_b + tkeys) / s))
+      // <= work / s + B, so s = ceil(work / (U - B)) fits; search the smallest fitting
+      // multiple of 32 between the two (the unit count does not grow with s).
       int lo = S + kTileKeys;
-      int hi = max(lo, max(a.min_split, round_tile((total_prefix + (U - B) - 1) / (U - B))));
+      int hi = max(lo, max(a.min_split, round_tile((work + (U - B) - 1) / (U - B))));
       // Invariant of both searches: lo - 32 does not fit, hi fits; uniform over the workgroup.
       if (B <= kFewRequests) {
         // Few requests: every thread counts the units of its own candidate length, so one
@@ -356,7 +364,7 @@ __device__ int plan_units(const PartialArgs& a, int g, bool publish, int* s_tmp,
           bool fits = false;
           if (tid < m) {
             int us = 0;
-            for (int k = 0; k < B; k++) us += max(1, (s_scr[k] + c - 1) / c);
+            for (int k = 0; k < B; k++) us += units_of(s_scr[k], c);
             fits = us <= U;
           }
           if (tid == 0) s_tmp[0] = kThreads;

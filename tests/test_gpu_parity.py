@@ -5,7 +5,6 @@ the workload configs run at full size.  Bitwise identities (fast path on/off,
 permuted pool, repeat runs, poisoned unused rows / workspace) need no tolerance.
 """
 
-import math
 
 import numpy as np
 import pytest
@@ -95,22 +94,31 @@ def test_small_parity(seed, prefix, t, h, tree, split):
     first = 0
     for b, rq in enumerate(plan["requests"]):
         assert rq["key_offset"] == offs[b] and rq["prefix_len"] == prefix[b]
-        assert rq["first_unit"] == first and rq["units"] == max(1, math.ceil(prefix[b] / plan["split_len"]))
+        assert rq["first_unit"] == first and rq["units"] == units_of(prefix[b], plan["split_len"], 0 if split else t)
         first += rq["units"]
         assert rq["error_bits"] == 0
     assert plan["total_units"] == first
     if split:
         assert plan["split_len"] == split
     else:
-        check_auto_split(prefix, plan["split_len"], plan["n_mtiles"])
+        check_auto_split(prefix, t, plan["split_len"], plan["n_mtiles"])
 
 
-def check_auto_split(prefix, s, n_mtiles):
+def units_of(p, s, t):
+    """Units of a request of p prefix tokens at split length s: under an automatic split its
+    t tree keys (in whole 32-key tiles) count as work of the last unit, which is the only
+    unit allowed past the prefix; under a fixed split (t = 0) only the prefix counts."""
+    tk = -(-t // 32) * 32
+    return max(1, min(-(-(p + tk) // s), -(-p // s) + 1))
+
+
+def check_auto_split(prefix, t, s, n_mtiles):
     """The automatic split length is the smallest multiple of 32 (at least 128) that keeps
     the unit count within one workgroup per CU per M tile (256 CUs), when the batch allows."""
     target = -(-256 // n_mtiles)
-    units = lambda x: sum(max(1, -(-p // x)) for p in prefix)
-    floor = max(128, -(-(-(-sum(prefix) // target)) // 32) * 32)
+    units = lambda x: sum(units_of(p, x, t) for p in prefix)
+    work = sum(prefix) + len(prefix) * (-(-t // 32) * 32)
+    floor = max(128, -(-(-(-work // target)) // 32) * 32)
     assert s % 32 == 0 and s >= floor
     if len(prefix) < target:
         assert units(s) <= target
@@ -132,7 +140,7 @@ def test_config_parity_sampled(i):
     cfg = synth.make_config(i)
     out, lse, v = run_gpu(cfg)
     plan = v.read_plan()
-    check_auto_split(cfg["prefix_lens"].tolist(), plan["split_len"], plan["n_mtiles"])
+    check_auto_split(cfg["prefix_lens"].tolist(), cfg["tree_nodes"], plan["split_len"], plan["n_mtiles"])
     rng = np.random.default_rng(100 + i)
     t = cfg["tree_nodes"]
     nodes = [(b, n) for b in range(cfg["batch"]) for n in sorted({0, t - 1, *rng.integers(0, t, 6).tolist()})]
