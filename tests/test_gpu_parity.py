@@ -174,6 +174,29 @@ def test_variant_parity(variant):
         assert np.abs(ref_out).max() > 1.0  # the needle dominates somewhere
 
 
+@pytest.mark.parametrize("variant", ["sharp", "needle_prefix", "needle_tree", "prefix0", "chain", "qzero"])
+def test_variant_parity_one_m_tile(variant):
+    # 64 rows in one M tile, three units; the needles raise a row's reference after its
+    # first tile (a restart of the unit)
+    cfg = synth.make_config(0, variant=variant)
+    out, lse, _ = run_gpu(cfg)
+    ref_out, ref_lse = run_oracle(cfg)
+    compare(out, lse, ref_out, ref_lse)
+
+
+@pytest.mark.parametrize("seed,prefix,t,h,split", [(40, [4000], 8, 8, 160), (41, [1, 95, 300, 2000], 5, 8, 0),
+                                                   (42, [700], 64, 1, 0), (43, [37, 0], 16, 4, 0)])
+def test_one_m_tile_many_tiles(seed, prefix, t, h, split):
+    # single-M-tile shapes with units of several tiles (odd and even counts), tree tiles,
+    # and a request with no prefix
+    cfg = synth.small_config(seed, batch=len(prefix), prefix=prefix, tree_nodes=t, heads=h,
+                             slots=max(4096, 2 * (sum(prefix) + len(prefix) * t)), tree="random", q_scale=1.0)
+    out, lse, v = run_gpu(cfg, split_tokens=split)
+    ref_out, ref_lse = run_oracle(cfg)
+    compare(out, lse, ref_out, ref_lse)
+    assert v.read_plan()["n_mtiles"] == 1
+
+
 def test_column_scales_keep_per_column_precision():
     """V columns span 2^-12 .. 2^12 (q scaled inversely, so the scores are those of the
     unscaled data).  Each output column divided by its scale must meet the bar of unscaled
