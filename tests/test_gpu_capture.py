@@ -1,7 +1,8 @@
-"""mlaverify_run under HIP graph capture: captured on a non-default stream, replayed
-several times with eager work in between, after the device inputs change in place;
-every replay must equal the eager result bit for bit.  Capture itself fails if run
-synchronises or allocates, so a successful capture also checks that."""
+"""mlaverify_run, mlaverify_relocate and mlaverify_accept under HIP graph capture: captured
+on a non-default stream, replayed several times with eager work in between, and after the
+device inputs change in place; every replay must equal the eager result bit for bit.
+Capture itself fails if a call synchronises or allocates, so a successful capture also
+checks that."""
 
 import numpy as np
 import pytest
@@ -59,3 +60,95 @@ def test_graph_replay_matches_eager(config):
     torch.cuda.synchronize()
     assert torch.equal(got_out, out) and torch.equal(got_lse, lse)
     assert not torch.equal(got_out, eager_out)
+
+
+def test_graph_replay_relocation():
+    # relocation under capture: each replay starts from the original pool and indices and
+    # must leave exactly the eager result (pool bytes and rewritten indices)
+    from gpu_util import i32
+
+    cfg = synth.defrag_config(5, batch=3, prefix=[700, 64, 1500], tree_nodes=12, heads=8, slots=8192)
+    d = upload(cfg)
+    v = verifier_for(cfg)
+    t = cfg["tree_nodes"]
+    dst = i32(cfg["dst_start"])
+    pool0, idx0 = d["pool"].clone(), d["kv_indices"].clone()
+    s = torch.cuda.Stream(device=DEV)
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        v.relocate(d["pool"], d["kv_indices"], d["prefix_lens"], dst, t, stream=s)
+    torch.cuda.synchronize()
+    assert v.read_device_errors() == 0
+    eager_pool, eager_idx = d["pool"].clone(), d["kv_indices"].clone()
+    assert not torch.equal(eager_idx, idx0)  # something moved
+    d["pool"].copy_(pool0)
+    d["kv_indices"].copy_(idx0)
+    torch.cuda.synchronize()
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        v.relocate(d["pool"], d["kv_indices"], d["prefix_lens"], dst, t, stream=s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        d["pool"].copy_(pool0)
+        d["kv_indices"].copy_(idx0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(d["pool"].view(torch.int16), eager_pool.view(torch.int16)), rep
+        assert torch.equal(d["kv_indices"], eager_idx), rep
+        # a replay over an already relocated batch moves nothing more
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(d["kv_indices"], eager_idx), rep
+    assert v.read_device_errors() == 0
+
+
+def test_graph_replay_acceptance():
+    # acceptance under capture: replays equal the eager result, with eager calls on the same
+    # handle in between (the walk leaves its workspace keys at zero), and follow new logits
+    from gpu_util import i32
+
+    cfg = synth.accept_config(4, batch=8, tree_nodes=64, vocab=131072)
+    b, t = cfg["tree_parent"].shape
+    v = mv_verifier_for_accept(b, t)
+    logits = torch.from_numpy(cfg["logits"]).to(DEV)
+    dt, par = i32(cfg["draft_tokens"]), i32(cfg["tree_parent"])
+    s = torch.cuda.Stream(device=DEV)
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        ref = [x.clone() for x in v.accept(logits, dt, par, stream=s)]
+    torch.cuda.synchronize()
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        outs = v.accept(logits, dt, par, stream=s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for o in outs:
+            o.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for o, r in zip(outs, ref):
+            assert torch.equal(o, r), rep
+        v.accept(logits, dt, par)  # eager work between replays
+        torch.cuda.synchronize()
+
+    # new logits in place: the replay must follow them
+    logits.copy_(torch.flip(logits, dims=[2]))
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    got = [o.clone() for o in outs]
+    eager = v.accept(logits, dt, par)
+    torch.cuda.synchronize()
+    for o, r in zip(got, eager):
+        assert torch.equal(o, r)
+    assert v.read_device_errors() == 0
+
+
+def mv_verifier_for_accept(b, t):
+    import mla_tree_verify_mlaverify_amd as mv
+
+    return mv.Verifier(num_heads=1, max_batch=b, max_tree_nodes=t, max_prefix_len=1, pool_slots=1, device=DEV)
