@@ -429,10 +429,171 @@ __device__ int plan_units(const PartialArgs& a, int g, bool publish, int* s_tmp,
   return total_units;
 }
 
+// Gathers of a unit with at most 64 rows in one M tile, run by waves 2 and 3, which hold
+// no rows, so that the compute waves issue none after tiles 0 and 1.  Rows pass through these waves' VGPRs
+// (plain non-temporal 16-byte loads, which reach a higher rate from HBM than LDS-DMA
+// gathers) on their way to LDS.  Helper thread hh covers keys hk and hk + 16 of a tile and
+// chunk slot hc of each of the 9 groups.  Two register stages hold tiles t+2 and t+3:
+// each tile's loads go out two iterations before it is written to LDS, so that two tiles
+// are in flight.  The loop mirrors the compute waves' barriers one for one from their
+// first scores on: that barrier, one per iteration, another on a restart (after the first
+// gathers again), and the final OR.  The function is kept out of line so that nothing of
+// the compute path is live in it, and its arguments come by value: a field read through
+// a reference is a flat load, and the waits for those would drain the stages.
+struct HelpState {
+  const int32_t* pidx;  // prefix part of the unit's index segment (as in the kernel)
+  const int32_t* tidx;  // tree part
+  int kbeg, npk, npt, ntiles, run_base, bad_index;
+};
+
+template <bool kPaged>
+__device__ __attribute__((noinline)) void gather_helper(const char* pool_in, int64_t row_stride_bytes,
+                                                        int64_t pool_slots, int T, int page_log2, int max_page,
+                                                        HelpState hs, char* smem, int* s_restart_in) {
+  typedef __attribute__((address_space(1))) const char gmem_char;
+  gmem_char* pool = (gmem_char*)pool_in;
+  int (*s_restart)[kWaves] = reinterpret_cast<int (*)[kWaves]>(s_restart_in);
+  typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+  lds_char* lds = (lds_char*)smem;
+  const int tid = threadIdx.x;
+  const int hh = tid - 2 * 64, hk = hh >> 3, hc = hh & 7;
+  const uint32_t wu = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ntiles = hs.ntiles, npt = hs.npt, npk = hs.npk, kbeg = hs.kbeg;
+  int bad = hs.bad_index;
+  const int pmask = (1 << page_log2) - 1;
+  auto page_slot = [&](int e, int pos) -> int {
+    return (uint32_t)e <= (uint32_t)max_page ? (e << page_log2) + (pos & pmask) : -1;
+  };
+  auto key_of = [&](int tl, int k) -> int {
+    const int nv = tl < npt ? min(kTileKeys, npk - tl * kTileKeys) : min(kTileKeys, T - (tl - npt) * kTileKeys);
+    return k < nv ? k : 0;
+  };
+  auto index_of = [&](int tl, int k) -> int {
+    if (kPaged && tl < npt)
+      return ((__attribute__((address_space(1))) const int32_t*)hs.pidx)[(kbeg + tl * kTileKeys + key_of(tl, k)) >> page_log2];
+    typedef __attribute__((address_space(1))) const int32_t gmem_i32;
+    gmem_i32* ip = (gmem_i32*)(tl < npt ? hs.pidx + tl * kTileKeys : hs.tidx + (tl - npt) * kTileKeys);
+    return ip[key_of(tl, k)];
+  };
+  auto slot_of = [&](int tl, int e, int k) -> int {
+    if (tl < npt && hs.run_base >= 0) return hs.run_base + tl * kTileKeys + key_of(tl, k);
+    if (kPaged && tl < npt) return page_slot(e, kbeg + tl * kTileKeys + key_of(tl, k));
+    return e;
+  };
+  auto row_of = [&](int idx) -> const char* {  // a slot outside the pool reads row 0 (and is flagged)
+    const bool oob = (uint32_t)idx >= (uint64_t)pool_slots;
+    bad |= oob ? 1 : 0;
+    return (const char*)(pool + (uint64_t)(oob ? 0u : (uint32_t)idx) * (uint64_t)row_stride_bytes);
+  };
+  // The first gathers of a pass, as every thread issues them: key tid / 8 of tiles 0 and 1.
+  auto dma_tiles01 = [&]() {
+    const int kt = tid >> 3;
+    const int kx = (tid & 7) ^ swz(kt);
+    for (int tl = 0; tl < 2 && tl < ntiles; tl++) {
+      const char* src = row_of(slot_of(tl, index_of(tl, kt), kt)) + kx * 16;
+      const uint32_t d = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds + tl * kTileBytes) + wu * 1024);
+      lds_dma16<0>(src + 0 * 128, d);
+      lds_dma16<1>(src + 1 * 128, d);
+      lds_dma16<2>(src + 2 * 128, d);
+      lds_dma16<3>(src + 3 * 128, d);
+      lds_dma16<4>(src + 4 * 128, d);
+      lds_dma16<5>(src + 5 * 128, d);
+      lds_dma16<6>(src + 6 * 128, d);
+      lds_dma16<7>(src + 7 * 128, d);
+      lds_dma16<8>(src + 8 * 128, d);
+    }
+  };
+  auto tile0_barrier = [&]() {  // start_scores: tile 0 has landed everywhere
+    if (ntiles > 1) {
+      __builtin_amdgcn_s_waitcnt(0x0F79);  // vmcnt(9)
+    } else {
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+    }
+    __syncthreads();
+  };
+  auto entries = [&](int (&en)[2], int tl) {
+#pragma unroll
+    for (int kk = 0; kk < 2; kk++) en[kk] = tl < ntiles ? index_of(tl, hk + 16 * kk) : 0;
+  };
+  auto rows = [&](u32x4 (&st)[18], int tl, const int (&en)[2]) {
+#pragma unroll
+    for (int kk = 0; kk < 2; kk++) {
+      const int k = hk + 16 * kk;
+      typedef __attribute__((address_space(1))) const u32x4 gmem_u32x4;
+      gmem_u32x4* src = (gmem_u32x4*)row_of(tl < ntiles ? slot_of(tl, en[kk], k) : 0) + (hc ^ swz(k));
+#pragma unroll
+      for (int j = 0; j < 9; j++) st[9 * kk + j] = __builtin_nontemporal_load(src + 8 * j);
+    }
+  };
+  auto write = [&](const u32x4 (&st)[18], int bufi) {
+#pragma unroll
+    for (int kk = 0; kk < 2; kk++) {
+      const int k = hk + 16 * kk;
+#pragma unroll
+      for (int j = 0; j < 9; j++)
+        *reinterpret_cast<lds_u32x4*>(lds + bufi * kTileBytes + j * 4096 + k * 128 + hc * 16) = st[9 * kk + j];
+    }
+  };
+  u32x4 st0[18], st1[18];
+  int en0[2], en1[2];  // index entries of the tile each stage loads next
+  // Stage 0 gets tile 2 and stage 1 tile 3, en0 and en1 the entries of tiles 4 and 5, in an
+  // order (rows, then the entries they lead to) that lets each wait below leave the other
+  // stage in flight, since loads complete in issue order.
+  auto start = [&]() {
+    int e2[2], e3[2];
+    entries(e2, 2);
+    entries(e3, 3);
+    rows(st0, 2, e2);
+    entries(en0, 4);
+    rows(st1, 3, e3);
+    entries(en1, 5);
+  };
+  // Iteration t: tile t+2 (in the stage of t's parity) goes to its buffer, which held tile
+  // t-1 and is free after this iteration's barrier; the stage then loads tile t+4.
+  auto step = [&](u32x4 (&st)[18], int (&en)[2], int tl) {
+    if (tl + 2 < ntiles) write(st, (tl + 2) % kTileBufs);
+    rows(st, tl + 4, en);
+    entries(en, tl + 6);
+  };
+  // The loop top: 0 = go on with tile t, 1 = the pass is over, 2 = it starts again.
+  int t = 0;
+  auto top = [&]() -> int {
+    __syncthreads();
+    const int* fl = s_restart[(t - 1) & 1];
+    if (t > 0 && (fl[0] | fl[1] | fl[2] | fl[3]) != 0) return 2;
+    return t == ntiles ? 1 : 0;
+  };
+  // One pass per outer iteration (a restart gathers tiles 0 and 1 again first).  The inner
+  // loop is unrolled by two, one stage per half, so that every path into its head leaves
+  // the loads in the same order (st0, en0, st1, en1) and the compiler's waits stay counted.
+  for (bool first = true;; first = false) {
+    if (!first) dma_tiles01();
+    tile0_barrier();
+    start();
+    t = 0;
+    int c;
+    for (;;) {
+      if ((c = top()) != 0) break;
+      step(st0, en0, t);
+      s_restart[t & 1][wu] = 0;
+      t++;
+      if ((c = top()) != 0) break;
+      step(st1, en1, t);
+      s_restart[t & 1][wu] = 0;
+      t++;
+    }
+    if (c == 1) break;
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // no load in flight when the workgroup ends
+  (void)__syncthreads_or(bad);         // the epilogue's
+}
+
 // kPaged: the prefix is addressed through a block table of 2^page_log2-slot pages (the
 // index segment holds page ids); otherwise through one slot per token.  kBigTree: T > 64,
-// so a row's ancestor mask takes kMaxTreeWords 64-bit words instead of one.
-template <bool kPaged, bool kBigTree>
+// so a row's ancestor mask takes kMaxTreeWords 64-bit words instead of one.  kHelp: at
+// most 64 rows in one M tile, so waves 2 and 3 hold no rows; they gather the tiles
+// (gather_helper) and the compute waves issue none after tiles 0 and 1.
+template <bool kPaged, bool kBigTree, bool kHelp>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_partial(PartialArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[kTileBufs * kTileBytes + kWaves * kQLdsBytes];
@@ -821,6 +982,14 @@ void k_partial(PartialArgs a) {
   }
 #pragma unroll
   for (int w = 0; w < kW; w++) anc[w] = (last && rvalid) ? s_m[(r / a.H) * kW + w] : ~0ull;
+  if constexpr (kHelp) {
+    if (wu >= 2) {
+      const HelpState hs = {pidx, tidx, kbeg, npk, npt, ntiles, run_base, bad_index};
+      gather_helper<kPaged>(reinterpret_cast<const char*>(a.pool), a.row_stride_bytes, a.pool_slots, a.T,
+                            a.page_log2, a.max_page, hs, smem, &s_restart[0][0]);
+      return;
+    }
+  }
   start_scores();
   for (;;) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's loads of tile t+1 landed
@@ -837,9 +1006,13 @@ void k_partial(PartialArgs a) {
     const SPre pre = s_pre(kb1);
     // Gathers of tile t+2 go to buffer b2 (on the last tiles they re-read pool row 0 into it;
     // nothing reads that buffer before the next barrier).
-    const char* pf_src = tile_src(t + 2 < ntiles ? slot_of(t + 2, idx_next) : 0);
-    const uint32_t pf_dst = tile_dst(b2);
-    if (t + 3 < ntiles) idx_next = load_index(t + 3);
+    const char* pf_src = nullptr;
+    uint32_t pf_dst = 0;
+    if (!kHelp) {
+      pf_src = tile_src(t + 2 < ntiles ? slot_of(t + 2, idx_next) : 0);
+      pf_dst = tile_dst(b2);
+      if (t + 3 < ntiles) idx_next = load_index(t + 3);
+    }
     const bool prev_flags = t > 0 && flags != 0;  // some wave raised its reference at tile t-1
     if (__builtin_expect(t == ntiles || prev_flags, 0)) {
       if (!prev_flags) break;
@@ -886,7 +1059,10 @@ void k_partial(PartialArgs a) {
     Soft so;
     f32x16 snext;
     if (__builtin_expect(t + 1 < ntiles, 1)) {
-      snext = s_chain(IntC<1>{}, IntC<1>{}, kb1, pf_src, pf_dst, sacc, nm, so, pre);
+      if constexpr (kHelp)  // the helper waves gather
+        snext = s_chain(IntC<-1>{}, IntC<1>{}, kb1, nullptr, 0u, sacc, nm, so, pre);
+      else
+        snext = s_chain(IntC<1>{}, IntC<1>{}, kb1, pf_src, pf_dst, sacc, nm, so, pre);
     } else {
 #pragma unroll
       for (int i = 0; i < 36; i++) soft_step(so, sacc, nm, i);
@@ -1040,14 +1216,19 @@ __global__ __launch_bounds__(256) void k_merge(MergeArgs a) {
 // ------------------------------------------------------------------------------------------
 hipError_t launch_partial(const PartialArgs& a, int grid, hipStream_t s) {
   const bool paged = a.page_log2 > 0, big = a.T > 64;
-  if (paged && big)
-    hipLaunchKernelGGL((k_partial<true, true>), dim3(grid), dim3(kThreads), 0, s, a);
+  const bool help = a.n_mtiles == 1 && a.M <= 2 * kRowsPerWave && !big;
+  if (help && paged)
+    hipLaunchKernelGGL((k_partial<true, false, true>), dim3(grid), dim3(kThreads), 0, s, a);
+  else if (help)
+    hipLaunchKernelGGL((k_partial<false, false, true>), dim3(grid), dim3(kThreads), 0, s, a);
+  else if (paged && big)
+    hipLaunchKernelGGL((k_partial<true, true, false>), dim3(grid), dim3(kThreads), 0, s, a);
   else if (paged)
-    hipLaunchKernelGGL((k_partial<true, false>), dim3(grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((k_partial<true, false, false>), dim3(grid), dim3(kThreads), 0, s, a);
   else if (big)
-    hipLaunchKernelGGL((k_partial<false, true>), dim3(grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((k_partial<false, true, false>), dim3(grid), dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((k_partial<false, false>), dim3(grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((k_partial<false, false, false>), dim3(grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -23,6 +23,16 @@ def test_agpr_audit_flags_compiler_agpr_use():
     assert len(bad) == 1 and "a3, v7" in bad[0]
 
 
+def test_agpr_audit_scopes_by_symbol_not_block_comment():
+    # the waves that run the gather helper hold no accumulator, so its AGPR uses pass; a block
+    # comment inside it ("; %bb.N:") does not end it, and the next symbol is audited again
+    text = ("_ZN3mlv13gather_helperILb0EEEvPKc:\n; %bb.46:\n\tglobal_load_dwordx4 a[0:3], v[20:21], off\n"
+            ".LBB3_2:\n\tv_accvgpr_read_b32 v1, a5\n"
+            "_ZN3mlv9k_partialILb0ELb0ELb1EEEvNS_11PartialArgsE:\n; %bb.0:\n\tv_accvgpr_write_b32 a7, v2\n")
+    bad = build.audit_agprs(text)
+    assert len(bad) == 1 and bad[0].startswith("_ZN3mlv9k_partial") and "a7, v2" in bad[0]
+
+
 def test_mfma_audit_flags_valu_write_of_operand():
     text = asm("v_mov_b32_e32 v4, v10", ";;#ASMSTART",
                "v_mfma_f32_32x32x16_bf16 a[0:15], v[2:5], v[6:9], a[0:15]", ";;#ASMEND")
