@@ -1142,30 +1142,37 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-// Row a.6.  kSplit workgroups per output row, each over 512/kSplit of its columns, so that
-// the grid fills the chip even when there are few rows.  The workgroup first finds
-// m = max_u lse_u (all threads loading at once), then wave w merges units w, w+4, ... with
-// kMergeDepth loads in flight (2 columns per lane) and the four waves add up through LDS.
+// Row a.6.  kSplit workgroups per output row, each over kCols = 512/kSplit of its columns,
+// so that the grid fills the chip even when there are few rows.  Every lane loads kPer
+// columns of a unit's partial: a group of kCols/kPer lanes covers one unit, so a wave takes
+// 64/(kCols/kPer) units at once and the workgroup kSlots = 4 * that many (slot s: units s,
+// s + kSlots, ...).  With few rows (kSplit = 8) lanes load 16 bytes and a wave takes 8
+// units; otherwise a wave covers the workgroup's columns and takes one unit.  The workgroup first finds m = max_u lse_u (all threads loading
+// at once); then each slot sums its units in steps of kMergeDepth, all of a step's loads in
+// flight, and the slots add up through LDS in a fixed order.
 // A NaN partial lse (a poisoned unit) makes the row NaN.
-template <int kSplit>
+template <int kSplit, int kPer>
 __global__ __launch_bounds__(256) void k_merge(MergeArgs a) {
-  constexpr int kCols = kVdim / kSplit;  // columns of this workgroup
-  constexpr int kPer = kCols / 64;       // columns per lane: 8, 4, 2 or 1
+  constexpr int kCols = kVdim / kSplit;   // columns of this workgroup
+  constexpr int kLanes = kCols / kPer;    // lanes per unit
+  constexpr int kGroups = 64 / kLanes;    // units per wave
+  constexpr int kSlots = kWaves * kGroups;
+  static_assert(kLanes * kGroups == 64 && kPer <= 8, "a wave covers whole units");
   typedef float fv __attribute__((ext_vector_type(kPer)));
-  __shared__ float s_acc[kWaves][kCols];
-  __shared__ float s_m[kWaves], s_z[kWaves];
+  typedef __bf16 hv __attribute__((ext_vector_type(kPer)));
+  __shared__ __attribute__((aligned(16))) float s_acc[kSlots][kCols];
+  __shared__ float s_m[kWaves], s_z[kSlots];
   const int row = blockIdx.x / kSplit;
   const int c0 = (blockIdx.x % kSplit) * kCols;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int cl = lane % kLanes, slot = w * kGroups + lane / kLanes;
   const int b = row / a.M, r = row - b * a.M;
   ReqPlan R = a.req[b];
   R.first_unit = min(max(R.first_unit, 0), a.units_cap);  // never index past the partial buffers
   R.units = min(R.units, a.units_cap - R.first_unit);
   const float* pl = a.part_lse + (size_t)R.first_unit * a.M + r;
-  const uint16_t* pob = a.part_o + ((size_t)R.first_unit * a.M + r) * kVdim + c0 + kPer * lane;
+  const uint16_t* pob = a.part_o + ((size_t)R.first_unit * a.M + r) * kVdim + c0 + kPer * cl;
   const size_t ustride = (size_t)a.M * kVdim;
-  typedef __bf16 hv __attribute__((ext_vector_type(kPer)));  // bf16 partial values
-  auto load_o = [&](int u) -> fv { return __builtin_convertvector(*reinterpret_cast<const hv*>(pob + u * ustride), fv); };
   // Reference m = max_u lse_u, with all 256 threads loading the unit lses at once.
   float m = -INFINITY;
   for (int u = tid; u < R.units; u += kThreads) m = fmaxf(m, pl[(size_t)u * a.M]);
@@ -1173,42 +1180,60 @@ __global__ __launch_bounds__(256) void k_merge(MergeArgs a) {
   if (lane == 0) s_m[w] = m;
   __syncthreads();
   m = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
-  // wave w takes units w, w+4, ... with kMergeDepth of them in flight; lane l holds columns
-  // c0 + kPer*l .. + kPer-1
   float z = 0.f;
   fv acc = {};
-  int u = w;
-  for (; u + (kMergeDepth - 1) * kWaves < R.units; u += kMergeDepth * kWaves) {
-    float wt[kMergeDepth];
-    fv o[kMergeDepth];
+  // One step: kMergeDepth units of this slot, all loads before any use so that no wait
+  // lands between them.  Only the last step of a slot can run past its last unit.  With
+  // several units per wave, that step re-reads the last unit in place of the missing ones
+  // (no branch between the loads) and drops them; with one, the rest go one unit at a
+  // time, which measured faster there.
+  auto step = [&](int u0, auto pred) {
+    constexpr bool kPred = decltype(pred)::value != 0;
+    float lu[kMergeDepth];
+    hv o[kMergeDepth];
 #pragma unroll
     for (int k = 0; k < kMergeDepth; k++) {
-      const float lu = pl[(size_t)(u + k * kWaves) * a.M];
-      wt[k] = (lu == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(lu - m);
-      o[k] = load_o(u + k * kWaves);
+      const int u = kPred ? min(u0 + k * kSlots, R.units - 1) : u0 + k * kSlots;
+      lu[k] = pl[(size_t)u * a.M];
+      o[k] = *reinterpret_cast<const hv*>(pob + u * ustride);
     }
 #pragma unroll
     for (int k = 0; k < kMergeDepth; k++) {
-      z += wt[k];
-      acc += wt[k] * o[k];
+      const bool live = !kPred || u0 + k * kSlots < R.units;
+      const float wt = (!live || lu[k] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(lu[k] - m);
+      const fv ov = __builtin_convertvector(o[k], fv);
+      z += wt;
+      acc += live ? wt * ov : fv{};
+    }
+  };
+  int u0 = slot;
+  for (; u0 + (kMergeDepth - 1) * kSlots < R.units; u0 += kMergeDepth * kSlots) step(u0, IntC<0>{});
+  if constexpr (kGroups > 1) {
+    if (u0 < R.units) step(u0, IntC<1>{});
+  } else {
+    for (; u0 < R.units; u0 += kSlots) {
+      const float lu = pl[(size_t)u0 * a.M];
+      const float wt = (lu == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(lu - m);
+      z += wt;
+      acc += wt * __builtin_convertvector(*reinterpret_cast<const hv*>(pob + u0 * ustride), fv);
     }
   }
-  for (; u < R.units; u += kWaves) {
-    const float lu = pl[(size_t)u * a.M];
-    const float wu = (lu == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(lu - m);
-    z += wu;
-    acc += wu * load_o(u);
-  }
-  *reinterpret_cast<fv*>(&s_acc[w][kPer * lane]) = acc;
-  if (lane == 0) s_z[w] = z;
+  *reinterpret_cast<fv*>(&s_acc[slot][kPer * cl]) = acc;
+  if (cl == 0) s_z[slot] = z;
   __syncthreads();
-  const float Z = (s_z[0] + s_z[1]) + (s_z[2] + s_z[3]);
+  float Z = 0.f;
+#pragma unroll
+  for (int q = 0; q < kSlots; q++) Z += s_z[q];
   const float inv = 1.0f / Z;
   for (int c = 2 * tid; c < kCols; c += 2 * kThreads) {
-    float o[2];
+    float o[2] = {0.f, 0.f};
 #pragma unroll
-    for (int e = 0; e < 2; e++) o[e] = ((s_acc[0][c + e] + s_acc[1][c + e]) + (s_acc[2][c + e] + s_acc[3][c + e])) * inv;
-    reinterpret_cast<uint32_t*>(a.out + (size_t)row * kVdim + c0 + c)[0] = bf16_rne_bits(o[0]) | (bf16_rne_bits(o[1]) << 16);
+    for (int q = 0; q < kSlots; q++) {
+      o[0] += s_acc[q][c];
+      o[1] += s_acc[q][c + 1];
+    }
+    reinterpret_cast<uint32_t*>(a.out + (size_t)row * kVdim + c0 + c)[0] =
+        bf16_rne_bits(o[0] * inv) | (bf16_rne_bits(o[1] * inv) << 16);
   }
   if (c0 == 0 && tid == 0) a.lse[row] = (m + __builtin_amdgcn_logf(Z)) * 0.69314718055994531f;
 }
@@ -1237,10 +1262,10 @@ hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
   const int rows = a.batch * a.M;
   const int split = rows * 8 <= kMergeBlocks ? 8 : rows * 4 <= kMergeBlocks ? 4 : rows * 2 <= kMergeBlocks ? 2 : 1;
   switch (split) {
-    case 8: hipLaunchKernelGGL(k_merge<8>, dim3(rows * 8), dim3(256), 0, s, a); break;
-    case 4: hipLaunchKernelGGL(k_merge<4>, dim3(rows * 4), dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL(k_merge<2>, dim3(rows * 2), dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL(k_merge<1>, dim3(rows), dim3(256), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((k_merge<8, 8>), dim3(rows * 8), dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((k_merge<4, 2>), dim3(rows * 4), dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k_merge<2, 4>), dim3(rows * 2), dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL((k_merge<1, 8>), dim3(rows), dim3(256), 0, s, a); break;
   }
   return hipGetLastError();
 }

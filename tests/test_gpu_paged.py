@@ -48,6 +48,30 @@ def test_paged_equals_its_expansion_and_oracle(seed, prefix, t, h, slots, page, 
     compare(a, la, ref_out, ref_lse)
 
 
+def test_paged_restart_on_the_helper_path():
+    # 64 rows in one M tile (the helper-wave path), fixed 256-token units, and in each request
+    # a dominant key at prefix position 100: the fourth tile of the first unit raises every
+    # row's reference, so the unit starts over and gathers its first two tiles through the
+    # block table again
+    cfg = synth.paged_config(9, batch=2, prefix=[1500, 700], tree_nodes=8, heads=8, slots=16384, page=16)
+    flat = expanded(cfg)
+    u = np.where(np.random.default_rng(9).integers(0, 2, size=synth.LATENT_DIM) == 1, 1.0, -1.0).astype(np.float32)
+    pool = cfg["pool"].copy()
+    for off in synth.request_offsets(cfg["prefix_lens"], cfg["tree_nodes"]):
+        pool[int(flat["kv_indices"][off + 100]), :synth.LATENT_DIM] = synth.f32_to_bf16_bits(2.0 * u)
+    q = synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(cfg["q"]) + 0.5 * u[None, None, :])
+    cfg = dict(cfg, pool=pool, q=q)
+    flat = dict(flat, pool=pool, q=q)
+    a, la, v = run_gpu(cfg, page_size=16, split_tokens=256)
+    b, lb, _ = run_gpu(flat, split_tokens=256)
+    assert np.array_equal(a, b) and np.array_equal(la, lb)
+    assert v.read_device_errors() == 0 and v.read_plan()["n_mtiles"] == 1
+    ref_out, ref_lse = orc.verify_attention(flat["q"], flat["pool"], flat["kv_indices"], flat["prefix_lens"],
+                                            flat["tree_parent"], flat["sm_scale"])
+    compare(a, la, ref_out, ref_lse)
+    assert np.abs(ref_out).max() > 1.0  # the needle dominates
+
+
 def test_consecutive_pages_take_the_fast_path():
     cfg = synth.paged_config(7, batch=2, prefix=[900, 260], tree_nodes=12, heads=8, slots=8192, page=64,
                              contiguous_pages=True)
