@@ -200,9 +200,12 @@ MLAVERIFY_API int mlaverify_tree_masks(const int32_t* tree_parent, int32_t batch
 
 /* Copies the work partition of the most recent run into host memory (synchronises
  * `stream`; for tests and reports, not for graphs).  Writes up to `capacity`
- * int32 values: [split_len, total_units, n_mtiles, then per request b:
- * key_offset_b, prefix_len_b, first_unit_b, units_b, prefix_error_bits_b]
- * (parent and index errors are reported by mlaverify_read_device_errors only).
+ * int32 values: [split_len, total_units, n_mtiles, fast_units, then per request b:
+ * key_offset_b, prefix_len_b, first_unit_b, units_b, prefix_error_bits_b], where
+ * fast_units counts the split units whose prefix slots formed one contiguous run and
+ * were read without the index table (the contiguous-run fast path; a unit with no
+ * prefix keys never counts).  Parent and index errors are reported by
+ * mlaverify_read_device_errors only.
  * Returns the number of values available (which may exceed capacity) or a
  * negative status. */
 MLAVERIFY_API int mlaverify_read_plan(mlaverify_t h, int32_t batch, void* stream, int32_t* host_out,

@@ -43,25 +43,122 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: install ROCm or set HIPCC")
 
 
+HELPER_MARK = "mlv-helper-waves"  # inline-asm comment at the entry of the helper waves' code
+
+
+def _functions(asm: str):
+    """(name, lines) of every function in the assembly."""
+    name, body = None, []
+    for line in asm.splitlines():
+        if re.match(r"[A-Za-z_][\w$.]*:", line) and not line.startswith(".L"):
+            if name:
+                yield name, body
+            name, body = line.split(":", 1)[0], []
+        elif name:
+            body.append(line)
+    if name:
+        yield name, body
+
+
+def _blocks(lines):
+    """Split a function body into basic blocks: [(label, [(line, in_asm)]), ...] and successor lists.
+    A block starts at a label or a '; %bb.N:' comment, or after a terminator.  The helper-wave
+    marker also starts a block (the code before it and after it are kept apart)."""
+    blocks, cur, in_asm = [], None, False
+
+    def new(label):
+        nonlocal cur
+        cur = [label, []]
+        blocks.append(cur)
+
+    new("<entry>")
+    for line in lines:
+        st = line.strip()
+        if st.startswith(";;#ASMSTART"):
+            in_asm = True
+            continue
+        if st.startswith(";;#ASMEND"):
+            in_asm = False
+            continue
+        m = re.match(r"(\.LBB\w+):", line) or re.match(r"; (%bb\.\d+):", line)
+        if m:
+            new(m.group(1))
+            continue
+        if in_asm and HELPER_MARK in st:
+            new("<helper>")
+            continue
+        if line.startswith("\t") and st and st[0].isalpha():
+            cur[1].append((st.split(";", 1)[0].strip(), in_asm))
+    labels = {b[0]: i for i, b in enumerate(blocks)}
+    succ = []
+    for i, (_, ins) in enumerate(blocks):
+        out, fall = [], True
+        for code, _asm in ins:
+            op, _, arg = code.partition(" ")
+            if op.startswith("s_cbranch") or op == "s_branch":
+                tgt = arg.strip()
+                if tgt in labels:
+                    out.append(labels[tgt])
+                if op == "s_branch":
+                    fall = False
+            elif op in ("s_endpgm", "s_setpc_b64"):
+                fall = False
+        if fall and i + 1 < len(blocks):
+            out.append(i + 1)
+        succ.append(out)
+    return blocks, succ
+
+
 def audit_agprs(asm: str) -> list[str]:
-    """AGPR uses outside inline asm in compiler output (each would clobber the accumulator)."""
-    bad, in_asm, func = [], False, "?"
+    """AGPR uses outside inline asm that the waves holding the output accumulator can execute.
+
+    Only the inline-asm MFMAs and accumulator moves may name an AGPR on those waves.  The
+    helper waves (which hold no rows) may: their code is entered at the HELPER_MARK marker,
+    and everything reachable from the kernel entry without passing the marker is audited.
+    Code the compiler shares between both paths is therefore audited too."""
+    bad = []
     agpr = re.compile(r"(?<![\w.])a(\d+|\[\d+:\d+\])")
+    for func, lines in _functions(asm):
+        blocks, succ = _blocks(lines)
+        helper = {i for i, b in enumerate(blocks) if b[0] == "<helper>"}
+        seen, stack = {0}, [0]
+        while stack:
+            i = stack.pop()
+            for j in succ[i]:
+                if j not in seen and j not in helper:
+                    seen.add(j)
+                    stack.append(j)
+        for i in sorted(seen):
+            for code, in_asm in blocks[i][1]:
+                if not in_asm and agpr.search(code):
+                    bad.append(f"{func}: {code}")
+    return bad
+
+
+def audit_m0(asm: str) -> list[str]:
+    """Instructions outside inline asm that name m0.  The LDS-DMA gathers set m0 inside their
+    asm statements and declare it clobbered, which the compiler does not honour for reserved
+    registers, so compiler-generated code must not keep anything live in m0."""
+    bad, in_asm, func = [], False, "?"
     for line in asm.splitlines():
         st = line.strip()
         if st.startswith(";;#ASMSTART"):
             in_asm = True
         elif st.startswith(";;#ASMEND"):
             in_asm = False
-        elif re.match(r"[A-Za-z_][\w$.]*:", line):  # a symbol (not a block comment or local label)
+        elif re.match(r"[A-Za-z_][\w$.]*:", line):
             func = line.split(":", 1)[0]
         elif not in_asm and line.startswith("\t") and st and st[0].isalpha():
             code = st.split(";", 1)[0]
-            # gather_helper runs only on waves that hold no rows and end right after it, so
-            # nothing there can meet the output accumulator
-            if agpr.search(code) and "gather_helper" not in func:
+            if re.search(r"\bm0\b", code):
                 bad.append(f"{func}: {code}")
     return bad
+
+
+def kernel_resources(asm: str) -> list[tuple[str, int, int]]:
+    """(kernel, private segment bytes, VGPR+AGPR count) of every kernel in the assembly."""
+    return [(m.group(1), int(m.group(2)), int(m.group(3))) for m in re.finditer(
+        r"\.name:\s+(\S+)[\s\S]*?\.private_segment_fixed_size:\s+(\d+)[\s\S]*?\.vgpr_count:\s+(\d+)", asm)]
 
 
 def _vgprs(operand: str) -> set[int]:
@@ -130,10 +227,19 @@ def check_device_code(src: str, verbose: bool = False) -> None:
     bad = audit_mfma_operands(out.stdout)
     if bad:
         raise RuntimeError("VALU write too close before an inline-asm MFMA in " + src + ":\n  " + "\n  ".join(bad[:20]))
+    bad = audit_m0(out.stdout)
+    if bad:
+        raise RuntimeError("compiler-generated m0 accesses in " + src + ":\n  " + "\n  ".join(bad[:20]))
+    res = kernel_resources(out.stdout)
+    if not res:
+        raise RuntimeError("no kernel metadata found in the assembly of " + src)
+    # spills to scratch are slow and, in the partial kernel, a sign that the register plan broke
+    spilled = [f"{n}: {b} B" for n, b, _ in res if b > 0]
+    if spilled:
+        raise RuntimeError("kernels with private (scratch) memory in " + src + ":\n  " + "\n  ".join(spilled))
     if verbose:
-        for m in re.finditer(r"\.name:\s+(\S+)[\s\S]*?\.private_segment_fixed_size:\s+(\d+)[\s\S]*?\.vgpr_count:\s+(\d+)",
-                             out.stdout):
-            print(f"{m.group(1)}: scratch {m.group(2)} B, vgpr+agpr {m.group(3)}", flush=True)
+        for n, b, v in res:
+            print(f"{n}: scratch {b} B, vgpr+agpr {v}", flush=True)
 
 
 def build(verbose: bool = False) -> str:

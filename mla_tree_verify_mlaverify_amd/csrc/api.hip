@@ -198,6 +198,7 @@ int mlaverify_run(mlaverify_t hd, int32_t batch, int32_t T, const void* q, const
   ka.req = reinterpret_cast<ReqPlan*>(hd->ws + L.req);
   ka.part_o = reinterpret_cast<uint16_t*>(hd->ws + L.part_o);
   ka.part_lse = reinterpret_cast<float*>(hd->ws + L.part_lse);
+  ka.unit_fast = reinterpret_cast<int32_t*>(hd->ws + L.unit_tab);
   ka.sticky_err = &ka.hdr->sticky_err;
   ka.pool_slots = c.pool_slots;
   ka.row_stride_bytes = c.kv_row_stride * 2;
@@ -315,27 +316,34 @@ int mlaverify_read_plan(mlaverify_t hd, int32_t batch, void* stream, int32_t* ho
   if (!hd || batch < 1 || batch > hd->cfg.max_batch || (capacity > 0 && !host_out) || capacity < 0)
     return MLAVERIFY_ERR_INVALID_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int needed = 3 + 5 * batch;
+  const int needed = 4 + 5 * batch;
   PlanHeader hdr;
-  ReqPlan* req = new (std::nothrow) ReqPlan[batch];
-  if (!req) return MLAVERIFY_ERR_NO_MEMORY;
-  bool ok = hipMemcpyAsync(&hdr, hd->ws + hd->L.hdr, sizeof(hdr), hipMemcpyDeviceToHost, s) == hipSuccess &&
-            hipMemcpyAsync(req, hd->ws + hd->L.req, sizeof(ReqPlan) * batch, hipMemcpyDeviceToHost, s) == hipSuccess &&
-            hipStreamSynchronize(s) == hipSuccess;
-  if (!ok) {
-    delete[] req;
-    return MLAVERIFY_ERR_HIP;
+  std::vector<ReqPlan> req;
+  std::vector<int32_t> fast;
+  try {
+    req.resize(batch);
+    fast.resize(hd->L.units_cap);
+  } catch (const std::bad_alloc&) {
+    return MLAVERIFY_ERR_NO_MEMORY;
   }
-  int32_t vals[3] = {hdr.split_len, hdr.total_units, hdr.n_mtiles};
-  for (int i = 0; i < 3 && i < capacity; i++) host_out[i] = vals[i];
+  bool ok = hipMemcpyAsync(&hdr, hd->ws + hd->L.hdr, sizeof(hdr), hipMemcpyDeviceToHost, s) == hipSuccess &&
+            hipMemcpyAsync(req.data(), hd->ws + hd->L.req, sizeof(ReqPlan) * batch, hipMemcpyDeviceToHost, s) ==
+                hipSuccess &&
+            hipMemcpyAsync(fast.data(), hd->ws + hd->L.unit_tab, sizeof(int32_t) * fast.size(), hipMemcpyDeviceToHost,
+                           s) == hipSuccess &&
+            hipStreamSynchronize(s) == hipSuccess;
+  if (!ok) return MLAVERIFY_ERR_HIP;
+  int32_t fast_units = 0;
+  for (int u = 0; u < hdr.total_units && u < (int)fast.size(); u++) fast_units += fast[u] != 0;
+  int32_t vals[4] = {hdr.split_len, hdr.total_units, hdr.n_mtiles, fast_units};
+  for (int i = 0; i < 4 && i < capacity; i++) host_out[i] = vals[i];
   for (int b = 0; b < batch; b++) {
     const int32_t rv[5] = {req[b].key_off, req[b].prefix_len, req[b].first_unit, req[b].units, (int32_t)req[b].err};
     for (int k = 0; k < 5; k++) {
-      const int pos = 3 + 5 * b + k;
+      const int pos = 4 + 5 * b + k;
       if (pos < capacity) host_out[pos] = rv[k];
     }
   }
-  delete[] req;
   return needed;
 }
 

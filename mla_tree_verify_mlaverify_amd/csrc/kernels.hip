@@ -114,11 +114,12 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast
 // scalar add); the caller passes the piece's global address.  Issued through asm so that the
 // compiler does not make every later LDS read wait for it; completion is awaited explicitly
 // (vmcnt(0) + barrier) before the tile is read.  The s_nop is the wait state between an M0
-// write and its LDS-DMA use.
+// write and its LDS-DMA use.  M0 is a reserved register that a clobber list cannot protect;
+// the build instead checks that no compiler-generated instruction uses it.
 template <int J>
 __device__ __forceinline__ void lds_dma16(const char* gaddr, uint32_t lds_base) {
   asm volatile("s_add_u32 m0, %1, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               ::"v"(gaddr), "s"(lds_base), "n"(J * 4096) : "m0");
+               ::"v"(gaddr), "s"(lds_base), "n"(J * 4096));
 }
 
 // Score MFMAs (bf16 32x32x16) are compiler builtins with VGPR accumulators (the library is
@@ -438,18 +439,16 @@ __device__ int plan_units(const PartialArgs& a, int g, bool publish, int* s_tmp,
 // are in flight.  The loop mirrors the compute waves' barriers one for one from their
 // first scores on: that barrier, one per iteration, another on a restart (after the first
 // gathers again), and the final OR.  The function is kept out of line so that nothing of
-// the compute path is live in it, and its arguments come by value: a field read through
-// a reference is a flat load, and the waits for those would drain the stages.
-struct HelpState {
-  const int32_t* pidx;  // prefix part of the unit's index segment (as in the kernel)
-  const int32_t* tidx;  // tree part
-  int kbeg, npk, npt, ntiles, run_base, bad_index;
-};
-
+// the compute path is live in it.  Its arguments are scalars passed by value: a field read
+// through a reference is a flat load, whose waits would drain the stages, and a struct
+// passed by value goes through the stack (private scratch).  pidx / tidx are the prefix and
+// tree parts of the unit's index segment, as in the kernel.
 template <bool kPaged>
-__device__ __attribute__((noinline)) void gather_helper(const char* pool_in, int64_t row_stride_bytes,
+[[noreturn]] __device__ __attribute__((always_inline)) inline void gather_helper(const char* pool_in, int64_t row_stride_bytes,
                                                         int64_t pool_slots, int T, int page_log2, int max_page,
-                                                        HelpState hs, char* smem, int* s_restart_in) {
+                                                        const int32_t* pidx, const int32_t* tidx, int kbeg, int npk,
+                                                        int npt, int ntiles, int run_base, int bad_index,
+                                                        char* smem, int* s_restart_in) {
   typedef __attribute__((address_space(1))) const char gmem_char;
   gmem_char* pool = (gmem_char*)pool_in;
   int (*s_restart)[kWaves] = reinterpret_cast<int (*)[kWaves]>(s_restart_in);
@@ -458,8 +457,7 @@ __device__ __attribute__((noinline)) void gather_helper(const char* pool_in, int
   const int tid = threadIdx.x;
   const int hh = tid - 2 * 64, hk = hh >> 3, hc = hh & 7;
   const uint32_t wu = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int ntiles = hs.ntiles, npt = hs.npt, npk = hs.npk, kbeg = hs.kbeg;
-  int bad = hs.bad_index;
+  int bad = bad_index;
   const int pmask = (1 << page_log2) - 1;
   auto page_slot = [&](int e, int pos) -> int {
     return (uint32_t)e <= (uint32_t)max_page ? (e << page_log2) + (pos & pmask) : -1;
@@ -470,13 +468,13 @@ __device__ __attribute__((noinline)) void gather_helper(const char* pool_in, int
   };
   auto index_of = [&](int tl, int k) -> int {
     if (kPaged && tl < npt)
-      return ((__attribute__((address_space(1))) const int32_t*)hs.pidx)[(kbeg + tl * kTileKeys + key_of(tl, k)) >> page_log2];
+      return ((__attribute__((address_space(1))) const int32_t*)pidx)[(kbeg + tl * kTileKeys + key_of(tl, k)) >> page_log2];
     typedef __attribute__((address_space(1))) const int32_t gmem_i32;
-    gmem_i32* ip = (gmem_i32*)(tl < npt ? hs.pidx + tl * kTileKeys : hs.tidx + (tl - npt) * kTileKeys);
+    gmem_i32* ip = (gmem_i32*)(tl < npt ? pidx + tl * kTileKeys : tidx + (tl - npt) * kTileKeys);
     return ip[key_of(tl, k)];
   };
   auto slot_of = [&](int tl, int e, int k) -> int {
-    if (tl < npt && hs.run_base >= 0) return hs.run_base + tl * kTileKeys + key_of(tl, k);
+    if (tl < npt && run_base >= 0) return run_base + tl * kTileKeys + key_of(tl, k);
     if (kPaged && tl < npt) return page_slot(e, kbeg + tl * kTileKeys + key_of(tl, k));
     return e;
   };
@@ -586,6 +584,9 @@ __device__ __attribute__((noinline)) void gather_helper(const char* pool_in, int
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // no load in flight when the workgroup ends
   (void)__syncthreads_or(bad);         // the epilogue's
+  // The helper waves end here.  Never returning also spares the call its callee-saved
+  // register spills (the waves hold nothing the kernel would need afterwards).
+  __builtin_amdgcn_endpgm();
 }
 
 // kPaged: the prefix is addressed through a block table of 2^page_log2-slot pages (the
@@ -748,6 +749,7 @@ void k_partial(PartialArgs a) {
   if (!plan_ok) {
     if (last) masks();  // its parents are still checked and reported
     poison();
+    if (tid == 0 && mt == 0) a.unit_fast[g] = 0;
     return;
   }
 
@@ -770,6 +772,7 @@ void k_partial(PartialArgs a) {
     }
     if (ok) run_base = run_first;
   }
+  if (tid == 0 && mt == 0) a.unit_fast[g] = run_base >= 0 ? 1 : 0;  // for the plan readback
   uint64_t anc[kW];  // this row's ancestor-mask words (filled before the first scores)
   u32x4 qf[kQReg];   // Q k-steps kept in VGPRs (filled after the first gathers)
   typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
@@ -984,9 +987,13 @@ void k_partial(PartialArgs a) {
   for (int w = 0; w < kW; w++) anc[w] = (last && rvalid) ? s_m[(r / a.H) * kW + w] : ~0ull;
   if constexpr (kHelp) {
     if (wu >= 2) {
-      const HelpState hs = {pidx, tidx, kbeg, npk, npt, ntiles, run_base, bad_index};
+      // From here on only the helper waves run; they hold no rows, so the build's register
+      // audit lets the compiler use AGPRs past this marker.
+      asm volatile("; mlv-helper-waves" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);  // keep the helper's code below the marker
       gather_helper<kPaged>(reinterpret_cast<const char*>(a.pool), a.row_stride_bytes, a.pool_slots, a.T,
-                            a.page_log2, a.max_page, hs, smem, &s_restart[0][0]);
+                            a.page_log2, a.max_page, pidx, tidx, kbeg, npk, npt, ntiles, run_base, bad_index, smem,
+                            &s_restart[0][0]);
       return;
     }
   }

@@ -67,6 +67,7 @@ struct PartialArgs {
   ReqPlan* req;
   uint16_t* part_o;      // [units, M, 512] unit-normalised partial outputs (bf16 bits)
   float* part_lse;       // [units, M] log2-domain lse of each partial (NaN: poisoned)
+  int32_t* unit_fast;    // [units] 1 if the unit's prefix was read as one contiguous run
   uint32_t* sticky_err;
   int64_t pool_slots;
   int64_t row_stride_bytes;

@@ -127,24 +127,15 @@ def check_auto_split(prefix, t, s, n_mtiles):
 
 # --------------------------------------------------------------------------- workload configs
 
-@pytest.mark.parametrize("i", [0, 1, 2, 5, 6])
+@pytest.mark.parametrize("i", [0, 1, 2, 3, 4, 5, 6])
 def test_config_parity_full(i):
-    cfg = synth.make_config(i)
-    out, lse, _ = run_gpu(cfg)
-    ref_out, ref_lse = run_oracle(cfg)
-    print(i, compare(out, lse, ref_out, ref_lse))
-
-
-@pytest.mark.parametrize("i", [3, 4])
-def test_config_parity_sampled(i):
+    """Every row of every workload, element by element (the 185k and batch workloads take the
+    oracle about a second each)."""
     cfg = synth.make_config(i)
     out, lse, v = run_gpu(cfg)
     plan = v.read_plan()
     check_auto_split(cfg["prefix_lens"].tolist(), cfg["tree_nodes"], plan["split_len"], plan["n_mtiles"])
-    rng = np.random.default_rng(100 + i)
-    t = cfg["tree_nodes"]
-    nodes = [(b, n) for b in range(cfg["batch"]) for n in sorted({0, t - 1, *rng.integers(0, t, 6).tolist()})]
-    ref_out, ref_lse = run_oracle(cfg, nodes=nodes)
+    ref_out, ref_lse = run_oracle(cfg)
     print(i, compare(out, lse, ref_out, ref_lse))
 
 
@@ -250,9 +241,74 @@ def test_row_stride_larger_than_row():
 
 def test_fast_path_is_bit_identical():
     cfg = synth.make_config(1, variant="contiguous")
-    a, la, _ = run_gpu(cfg)
-    b, lb, _ = run_gpu(cfg, flags=mv.FLAG_NO_FASTPATH)
+    a, la, v = run_gpu(cfg)
+    assert v.read_plan()["fast_units"] > 0
+    b, lb, v = run_gpu(cfg, flags=mv.FLAG_NO_FASTPATH)
+    assert v.read_plan()["fast_units"] == 0
     assert np.array_equal(a, b) and np.array_equal(la, lb)
+
+
+def prefix_units(plan):
+    """Units that hold prefix keys (a request's units all do, except a last one past its prefix)."""
+    n = 0
+    for rq in plan["requests"]:
+        s = plan["split_len"]
+        n += min(rq["units"], -(-rq["prefix_len"] // s))
+    return n
+
+
+@pytest.mark.parametrize("variant", ["contiguous", "sorted"])
+def test_fast_path_on_long_units(variant):
+    """The 65k workload with its indices defragmented into one run, or only sorted: units of
+    about a thousand keys, so the run check also takes its rounds past the first 256 keys.
+    Each unit of the run takes the fast path; sorted indices (gaps between slots) take none.
+    Both match the oracle and are bit-identical to the row-by-row gathers."""
+    cfg = synth.make_config(2, variant=variant)
+    out, lse, v = run_gpu(cfg)
+    plan = v.read_plan()
+    assert plan["split_len"] > 256
+    expect = prefix_units(plan) if variant == "contiguous" else 0
+    assert plan["fast_units"] == expect, (plan["fast_units"], expect)
+    ref_out, ref_lse = run_oracle(cfg)
+    print(variant, compare(out, lse, ref_out, ref_lse))
+    b, lb, v2 = run_gpu(cfg, flags=mv.FLAG_NO_FASTPATH)
+    assert v2.read_plan()["fast_units"] == 0
+    assert np.array_equal(out, b) and np.array_equal(lse, lb)
+
+
+@pytest.mark.parametrize("split", [1024, 0])
+def test_fast_path_rejects_broken_runs(split):
+    """A contiguous prefix with single slots replaced by a slot outside the run, at unit key
+    100 (the check's first round), 300 and 700 (later rounds), a unit's last key, and the
+    request's last prefix key.  Exactly the units holding a break leave the fast path; the
+    output matches the oracle and the row-by-row gathers bit for bit."""
+    prefix, t = 20517, 64  # 512 rows: the automatic split is then longer than 256 keys
+    cfg = synth.small_config(50, batch=1, prefix=[prefix], tree_nodes=t, heads=8, slots=65536, tree="random",
+                             q_scale=1.0)
+    cfg = synth.apply_variant(cfg, "contiguous")
+    v0 = verifier_for(cfg, split_tokens=split)
+    run_gpu(cfg, v0)
+    plan = v0.read_plan()
+    s = plan["split_len"]
+    assert s > 256 and plan["fast_units"] == prefix_units(plan)
+    last = (prefix - 1) // s  # the last unit holding prefix keys
+    base = int(cfg["kv_indices"][0])
+    assert base >= 8 and last > 5, "free slots below the run, and enough units"
+    breaks = {1: 100, 2: 300, 4: s - 1, 5: min(700, s - 2), last: prefix - 1 - last * s}
+    broken = dict(cfg)
+    idx = cfg["kv_indices"].copy()
+    for j, (u, k) in enumerate(sorted(breaks.items())):
+        assert 0 <= k < s and u * s + k < prefix
+        idx[u * s + k] = base - 1 - j  # a free slot below the run (its row is ordinary data)
+    broken["kv_indices"] = idx
+    out, lse, v = run_gpu(broken, split_tokens=split)
+    plan = v.read_plan()
+    assert plan["split_len"] == s
+    assert plan["fast_units"] == prefix_units(plan) - len(breaks), plan
+    ref_out, ref_lse = run_oracle(broken)
+    compare(out, lse, ref_out, ref_lse)
+    b, lb, _ = run_gpu(broken, split_tokens=split, flags=mv.FLAG_NO_FASTPATH)
+    assert np.array_equal(out, b) and np.array_equal(lse, lb)
 
 
 def test_permuted_pool_is_bit_identical():
