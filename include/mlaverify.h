@@ -134,6 +134,31 @@ MLAVERIFY_API int mlaverify_run(mlaverify_t h, int32_t batch, int32_t tree_nodes
                                 const int32_t* prefix_lens, const int32_t* tree_parent,
                                 void* out, float* lse, void* stream);
 
+/* Bytes of the static device workspace behind mlaverify_run_static (48 MiB per GPU). */
+#define MLAVERIFY_STATIC_SCRATCH_BYTES ((size_t)48 << 20)
+
+/* For callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  The same verify pass as mlaverify_run
+ * (same kernels, same results bit for bit), without a handle or a caller workspace: the
+ * workspace is a static device array of MLAVERIFY_STATIC_SCRATCH_BYTES that the library
+ * holds on every GPU it runs on until the process ends.  The call allocates nothing: no
+ * hipMalloc, no hipFree, no allocating library routine.  Its first call on a device looks
+ * up that device's copy of the array (hipGetSymbolAddress, with the device current).
+ * cfg: as for mlaverify_create (validated on every call; pure host work).  The other
+ * arguments are those of mlaverify_run, on the current device.  A call whose partial
+ * results need more than MLAVERIFY_STATIC_SCRATCH_BYTES returns MLAVERIFY_ERR_WORKSPACE
+ * and enqueues nothing: that is (H * T) rows x (units + batch) x 1028 bytes plus a few KB,
+ * where units = ceil(256 / ceil(H * T / 128)) under the automatic split, about 34 MB for
+ * one request of 64 nodes and 8 heads.  Every call on a GPU shares that GPU's array, so
+ * calls that overlap in time on one GPU (different streams, or different host threads
+ * without ordering) race and give wrong results; order them on one stream.  Data errors
+ * show as NaN rows exactly as for mlaverify_run; their sticky bits are not readable here.
+ * Never synchronises or copies to the host: graph-capturable. */
+MLAVERIFY_API int mlaverify_run_static(const mlaverify_config* cfg, int32_t batch, int32_t tree_nodes,
+                                       const void* q, const void* kv_pool, const int32_t* kv_indices,
+                                       const int32_t* prefix_lens, const int32_t* tree_parent, void* out,
+                                       float* lse, void* stream);
+
 /* Tier-1 KV relocation (live defragmentation of prefix rows).  The "Chunk 66.0"
  * summary calls for K/V defragmentation of the scattered page_size=1 pool; the
  * "Chunk 66.1" summary keeps a request's KV contiguous when it is allocated (Tier 0)

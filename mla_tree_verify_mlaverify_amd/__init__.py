@@ -17,6 +17,7 @@ from .binding import (  # noqa: F401
     Verifier,
     load_library,
     make_config,
+    run_static,
     status_string,
     tree_masks,
     validate_config,

@@ -42,6 +42,7 @@ EXPORTED = (
     "mlaverify_workspace_bytes",
     "mlaverify_create",
     "mlaverify_run",
+    "mlaverify_run_static",
     "mlaverify_relocate",
     "mlaverify_accept",
     "mlaverify_tree_masks",
@@ -98,6 +99,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.mlaverify_create.restype = ctypes.c_int
     lib.mlaverify_run.argtypes = [c_void_p, c_int32, c_int32] + [c_void_p] * 8
     lib.mlaverify_run.restype = ctypes.c_int
+    lib.mlaverify_run_static.argtypes = [cfg_p, c_int32, c_int32] + [c_void_p] * 8
+    lib.mlaverify_run_static.restype = ctypes.c_int
     lib.mlaverify_relocate.argtypes = [c_void_p, c_int32, c_int32] + [c_void_p] * 5
     lib.mlaverify_relocate.restype = ctypes.c_int
     lib.mlaverify_accept.argtypes = [c_void_p, c_int32, c_int32, c_int32] + [c_void_p] * 7
@@ -309,6 +312,35 @@ class Verifier:
         if rc != OK:
             raise MlaVerifyError(rc, "mlaverify_read_device_errors")
         return flags.value
+
+
+STATIC_SCRATCH_BYTES = 48 << 20
+
+
+def run_static(cfg: MlaVerifyConfig, q, kv_pool, kv_indices, prefix_lens, tree_parent, out, lse, stream=None) -> None:
+    """The verify pass over the library's static workspace (mlaverify_run_static): no handle,
+    nothing allocated by the library or here; out and lse are written in place."""
+    lib = load_library()
+    if tree_parent.dim() != 2:
+        raise ValueError("tree_parent must be [batch, T]")
+    b, t = tree_parent.shape
+    h = cfg.num_heads
+    dev = q.device
+    _check(tree_parent, "tree_parent", torch.int32, (b, t), dev)
+    _check(q, "q", torch.bfloat16, (b * t, h, LATENT_DIM), dev)
+    _check(prefix_lens, "prefix_lens", torch.int32, (b,), dev)
+    _check(kv_indices, "kv_indices", torch.int32, None, dev)
+    if kv_indices.dim() != 1:
+        raise ValueError("kv_indices must be 1-D")
+    _check(kv_pool, "kv_pool", torch.bfloat16, (cfg.pool_slots, cfg.kv_row_stride), dev)
+    _check(out, "out", torch.bfloat16, (b * t, h, V_DIM), dev)
+    _check(lse, "lse", torch.float32, (b * t, h), dev)
+    with torch.cuda.device(dev):
+        rc = lib.mlaverify_run_static(ctypes.byref(cfg), b, t, q.data_ptr(), kv_pool.data_ptr(), kv_indices.data_ptr(),
+                                      prefix_lens.data_ptr(), tree_parent.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                      _stream_handle(stream))
+    if rc != OK:
+        raise MlaVerifyError(rc, "mlaverify_run_static")
 
 
 def tree_masks(tree_parent: torch.Tensor, stream=None):

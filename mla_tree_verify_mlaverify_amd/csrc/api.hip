@@ -5,6 +5,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -93,6 +94,130 @@ void release_profile(mlaverify_handle* hd) {
 }
 }  // namespace
 
+namespace {
+
+// Host checks shared by the entry points of the verify pass.
+int check_run_args(const mlaverify_config& c, int batch, int T, const void* q, const void* kv_pool,
+                   const int32_t* kv_indices, const int32_t* prefix_lens, const int32_t* tree_parent, const void* out,
+                   const float* lse) {
+  if (batch < 1 || batch > c.max_batch || T < 1 || T > c.max_tree_nodes) return MLAVERIFY_ERR_INVALID_ARG;
+  if (!q || !kv_pool || !kv_indices || !prefix_lens || !tree_parent || !out || !lse) return MLAVERIFY_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(kv_pool, 16) || !aligned(out, 16)) return MLAVERIFY_ERR_INVALID_ARG;
+  if (!aligned(kv_indices, 4) || !aligned(prefix_lens, 4) || !aligned(tree_parent, 4) || !aligned(lse, 4))
+    return MLAVERIFY_ERR_INVALID_ARG;
+  return MLAVERIFY_OK;
+}
+
+// The workspace areas one verify pass uses.
+struct RunAreas {
+  PlanHeader* hdr;
+  ReqPlan* req;
+  int32_t* unit_fast;
+  float* part_lse;
+  uint16_t* part_o;
+};
+
+// Offsets of those areas for one call of `batch` requests of T nodes; returns the bytes used.
+struct RunOffsets {
+  size_t hdr, req, unit_tab, part_lse, part_o;
+};
+size_t run_offsets(const mlaverify_config& c, int batch, int T, RunOffsets* o) {
+  const int units = units_for(c, batch, T);
+  const size_t rows = (size_t)units * c.num_heads * T;
+  size_t off = 0;
+  o->hdr = off;      off = align_up(off + sizeof(PlanHeader));
+  o->req = off;      off = align_up(off + sizeof(ReqPlan) * (size_t)batch);
+  o->unit_tab = off; off = align_up(off + sizeof(int32_t) * (size_t)units);
+  o->part_lse = off; off = align_up(off + sizeof(float) * rows);
+  o->part_o = off;   off = align_up(off + sizeof(uint16_t) * rows * kVdim);
+  return off;
+}
+
+// Enqueues the two kernels of one verify pass (plan + partials, then the merge) over the
+// workspace areas w; records the profiling events ev[0..2] around them when ev is given.
+int enqueue_run(const mlaverify_config& c, const RunAreas& w, int batch, int T, const void* q, const void* kv_pool,
+                const int32_t* kv_indices, const int32_t* prefix_lens, const int32_t* tree_parent, void* out,
+                float* lse, hipStream_t s, hipEvent_t* ev) {
+  const int n_mt = mtiles_for(c.num_heads, T);
+  const int units_grid = units_for(c, batch, T);
+  const int M = c.num_heads * T;
+
+  PartialArgs ka;
+  ka.q = static_cast<const uint16_t*>(q);
+  ka.pool = static_cast<const uint16_t*>(kv_pool);
+  ka.kv_indices = kv_indices;
+  ka.prefix_lens = prefix_lens;
+  ka.tree_parent = tree_parent;
+  ka.hdr = w.hdr;
+  ka.req = w.req;
+  ka.part_o = w.part_o;
+  ka.part_lse = w.part_lse;
+  ka.unit_fast = w.unit_fast;
+  ka.sticky_err = &w.hdr->sticky_err;
+  ka.pool_slots = c.pool_slots;
+  ka.row_stride_bytes = c.kv_row_stride * 2;
+  ka.batch = batch;
+  ka.T = T;
+  ka.H = c.num_heads;
+  ka.M = M;
+  ka.n_mtiles = n_mt;
+  ka.max_prefix = c.max_prefix_len;
+  ka.split_fixed = c.split_tokens;
+  ka.target_units = target_units_for(n_mt);
+  ka.min_split = kMinSplit;
+  ka.units_cap = units_grid;
+  ka.scale_log2 = c.sm_scale * 1.4426950408889634f;
+  ka.flags = c.flags;
+  ka.page_log2 = page_log2(c.page_size);
+  ka.max_page = (int32_t)((c.pool_slots - 1) >> ka.page_log2);
+  ka.group_xcd = units_grid >= 8 ? 1 : 0;  // too few units to fill 8 XCDs one unit apiece
+
+  MergeArgs ma;
+  ma.req = ka.req;
+  ma.part_o = ka.part_o;
+  ma.part_lse = ka.part_lse;
+  ma.out = static_cast<uint16_t*>(out);
+  ma.lse = lse;
+  ma.batch = batch;
+  ma.M = M;
+  ma.units_cap = units_grid;
+
+  const int grid = n_mt * (int)(cdiv(units_grid, 8) * 8);
+  if (ev && hipEventRecord(ev[0], s) != hipSuccess) return MLAVERIFY_ERR_HIP;
+  if (launch_partial(ka, grid, s) != hipSuccess) return MLAVERIFY_ERR_HIP;
+  if (ev && hipEventRecord(ev[1], s) != hipSuccess) return MLAVERIFY_ERR_HIP;
+  if (launch_merge(ma, s) != hipSuccess) return MLAVERIFY_ERR_HIP;
+  if (ev && hipEventRecord(ev[2], s) != hipSuccess) return MLAVERIFY_ERR_HIP;
+  return MLAVERIFY_OK;
+}
+
+// ---- Workspace of mlaverify_run_static: a file-scope device array, one copy per GPU, held
+// until the process ends.  Host code never passes `scratch` itself to a kernel or a copy (in
+// host code that name is a host-side stand-in, not a device address): its address on each
+// device is taken once, with that device current, and kept in g_scratch_ptr.
+constexpr size_t kStaticScratchBytes = MLAVERIFY_STATIC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch`.
+int static_scratch(char** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MLAVERIFY_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MLAVERIFY_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MLAVERIFY_ERR_HIP;
+    g_scratch_ptr[dev] = static_cast<char*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return MLAVERIFY_OK;
+}
+
+}  // namespace
+
 // Launches go to the handle's device only: its workspace lives there.
 static bool on_handle_device(const mlaverify_handle* hd) {
   int dev = -1;
@@ -177,67 +302,37 @@ int mlaverify_run(mlaverify_t hd, int32_t batch, int32_t T, const void* q, const
   if (!hd) return MLAVERIFY_ERR_INVALID_ARG;
   if (!on_handle_device(hd)) return MLAVERIFY_ERR_INVALID_ARG;
   const mlaverify_config& c = hd->cfg;
-  if (batch < 1 || batch > c.max_batch || T < 1 || T > c.max_tree_nodes) return MLAVERIFY_ERR_INVALID_ARG;
-  if (!q || !kv_pool || !kv_indices || !prefix_lens || !tree_parent || !out || !lse) return MLAVERIFY_ERR_INVALID_ARG;
-  if (!aligned(q, 16) || !aligned(kv_pool, 16) || !aligned(out, 16)) return MLAVERIFY_ERR_INVALID_ARG;
-  if (!aligned(kv_indices, 4) || !aligned(prefix_lens, 4) || !aligned(tree_parent, 4) || !aligned(lse, 4))
-    return MLAVERIFY_ERR_INVALID_ARG;
-  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int v = check_run_args(c, batch, T, q, kv_pool, kv_indices, prefix_lens, tree_parent, out, lse);
+  if (v != MLAVERIFY_OK) return v;
   const Layout& L = hd->L;
-  const int n_mt = mtiles_for(c.num_heads, T);
-  const int units_grid = units_for(c, batch, T);
-  const int M = c.num_heads * T;
-
-  PartialArgs ka;
-  ka.q = static_cast<const uint16_t*>(q);
-  ka.pool = static_cast<const uint16_t*>(kv_pool);
-  ka.kv_indices = kv_indices;
-  ka.prefix_lens = prefix_lens;
-  ka.tree_parent = tree_parent;
-  ka.hdr = reinterpret_cast<PlanHeader*>(hd->ws + L.hdr);
-  ka.req = reinterpret_cast<ReqPlan*>(hd->ws + L.req);
-  ka.part_o = reinterpret_cast<uint16_t*>(hd->ws + L.part_o);
-  ka.part_lse = reinterpret_cast<float*>(hd->ws + L.part_lse);
-  ka.unit_fast = reinterpret_cast<int32_t*>(hd->ws + L.unit_tab);
-  ka.sticky_err = &ka.hdr->sticky_err;
-  ka.pool_slots = c.pool_slots;
-  ka.row_stride_bytes = c.kv_row_stride * 2;
-  ka.batch = batch;
-  ka.T = T;
-  ka.H = c.num_heads;
-  ka.M = M;
-  ka.n_mtiles = n_mt;
-  ka.max_prefix = c.max_prefix_len;
-  ka.split_fixed = c.split_tokens;
-  ka.target_units = target_units_for(n_mt);
-  ka.min_split = kMinSplit;
-  ka.units_cap = units_grid;
-  ka.scale_log2 = c.sm_scale * 1.4426950408889634f;
-  ka.flags = c.flags;
-  ka.page_log2 = page_log2(c.page_size);
-  ka.max_page = (int32_t)((c.pool_slots - 1) >> ka.page_log2);
-  ka.group_xcd = units_grid >= 8 ? 1 : 0;  // too few units to fill 8 XCDs one unit apiece
-
-  MergeArgs ma;
-  ma.req = ka.req;
-  ma.part_o = ka.part_o;
-  ma.part_lse = ka.part_lse;
-  ma.out = static_cast<uint16_t*>(out);
-  ma.lse = lse;
-  ma.batch = batch;
-  ma.M = M;
-  ma.units_cap = units_grid;
-
-  const int grid = n_mt * (int)(cdiv(units_grid, 8) * 8);
+  const RunAreas w = {reinterpret_cast<PlanHeader*>(hd->ws + L.hdr), reinterpret_cast<ReqPlan*>(hd->ws + L.req),
+                      reinterpret_cast<int32_t*>(hd->ws + L.unit_tab), reinterpret_cast<float*>(hd->ws + L.part_lse),
+                      reinterpret_cast<uint16_t*>(hd->ws + L.part_o)};
   hipEvent_t* ev = nullptr;
   if (hd->prof_runs < hd->prof_max) ev = &hd->prof_events[3 * hd->prof_runs++];
-  if (ev && hipEventRecord(ev[0], s) != hipSuccess) return MLAVERIFY_ERR_HIP;
-  if (launch_partial(ka, grid, s) != hipSuccess) return MLAVERIFY_ERR_HIP;
-  if (ev && hipEventRecord(ev[1], s) != hipSuccess) return MLAVERIFY_ERR_HIP;
-  if (launch_merge(ma, s) != hipSuccess) return MLAVERIFY_ERR_HIP;
-  if (ev && hipEventRecord(ev[2], s) != hipSuccess) return MLAVERIFY_ERR_HIP;
-  hd->last_batch = batch;
-  return MLAVERIFY_OK;
+  const int rc = enqueue_run(c, w, batch, T, q, kv_pool, kv_indices, prefix_lens, tree_parent, out, lse,
+                             static_cast<hipStream_t>(stream), ev);
+  if (rc == MLAVERIFY_OK) hd->last_batch = batch;
+  return rc;
+}
+
+int mlaverify_run_static(const mlaverify_config* c, int32_t batch, int32_t T, const void* q, const void* kv_pool,
+                         const int32_t* kv_indices, const int32_t* prefix_lens, const int32_t* tree_parent,
+                         void* out, float* lse, void* stream) {
+  const int v = mlaverify_validate_config(c);
+  if (v != MLAVERIFY_OK) return v;
+  const int a = check_run_args(*c, batch, T, q, kv_pool, kv_indices, prefix_lens, tree_parent, out, lse);
+  if (a != MLAVERIFY_OK) return a;
+  RunOffsets o;
+  if (run_offsets(*c, batch, T, &o) > kStaticScratchBytes) return MLAVERIFY_ERR_WORKSPACE;
+  char* base = nullptr;
+  const int sp = static_scratch(&base);
+  if (sp != MLAVERIFY_OK) return sp;
+  const RunAreas w = {reinterpret_cast<PlanHeader*>(base + o.hdr), reinterpret_cast<ReqPlan*>(base + o.req),
+                      reinterpret_cast<int32_t*>(base + o.unit_tab), reinterpret_cast<float*>(base + o.part_lse),
+                      reinterpret_cast<uint16_t*>(base + o.part_o)};
+  return enqueue_run(*c, w, batch, T, q, kv_pool, kv_indices, prefix_lens, tree_parent, out, lse,
+                     static_cast<hipStream_t>(stream), nullptr);
 }
 
 int mlaverify_relocate(mlaverify_t hd, int32_t batch, int32_t T, void* kv_pool, int32_t* kv_indices,

@@ -114,3 +114,14 @@ def test_run_rejects_null_handle(lib):
 def test_missing_library_fails_loudly(tmp_path):
     with pytest.raises(ImportError):
         binding.load_library(str(tmp_path / "nope.so"))
+
+
+def test_run_static_refuses_oversize_calls_before_any_device_work(lib):
+    # 128 heads x 256 nodes needs 2 x 32,768 rows of partials (about 67 MB), more than the
+    # static workspace: refused on the host, so no GPU is needed for this check.  The device
+    # pointers are never dereferenced.
+    cfg = binding.make_config(128, 1, 256, 64, 1024)
+    fake = [ctypes.c_void_p(1 << 20)] * 8
+    assert lib.mlaverify_run_static(ctypes.byref(cfg), 1, 256, *fake) == binding.ERR_WORKSPACE
+    assert lib.mlaverify_run_static(None, 1, 256, *fake) == binding.ERR_INVALID_ARG
+    assert lib.mlaverify_run_static(ctypes.byref(cfg), 2, 256, *fake) == binding.ERR_INVALID_ARG  # batch > max_batch
