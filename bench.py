@@ -6,13 +6,19 @@ workload, with its inputs resident in HBM and the caches flushed before each cal
 decode steps.  Prints one JSON line: µs per call, KV GB/s, the partial
 kernel's roofline and, unless --no-cpu, the CPU oracle timed on the host.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--config 3] [--warm] [--no-cpu]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config 3] [--warm] [--no-cpu]
+
+The default run times the 185k-token workload (the headline line) and then, with the same
+protocol, every other seeded workload (`per_config`), the measured stream bandwidth of the
+1 GiB flush kernel (`hbm_stream_gbs`, so that %HBM is also given against it) and the
+scattered-read probe on the headline's rows (`gather_probe_gbs`).
 
 With --op relocate it measures Tier-1 relocation instead: one call moves a 185,000-row
 prefix, scattered over the lower half of a 524,288-slot pool, into one run in the upper
 half (the index list is restored before each call, outside the timed region).  With
 --op accept it measures greedy acceptance of a 64-node tree over fp32 logits of a
-131,072-token vocabulary.
+131,072-token vocabulary.  With --op gather it runs the scattered-row read probe alone: the
+185k workload's prefix rows read into registers and into LDS at 256-2,048 workgroups.
 """
 
 from __future__ import annotations
@@ -307,11 +313,89 @@ def bench_accept(args) -> int:
     return 0
 
 
+GATHER_METRIC = "scattered KV-row gather GB/s (185,000 rows of 1,152 B from a 262,144-slot pool, caches flushed)"
+GATHER_GRIDS = (256, 512, 1024, 2048)
+
+
+def gather_probe(cfg: dict, flush, grids=GATHER_GRIDS, reps: int = 10) -> dict:
+    """Rate of the probe kernels (mlaverify_probe_gather) reading the workload's prefix rows through
+    each 16-byte load path, per grid size: {"register": {grid: GB/s}, "lds": {...}} counting the
+    rows' 1,152 bytes (the index list adds 4 bytes per row)."""
+    import torch
+
+    import mla_tree_verify_mlaverify_amd as mv
+
+    dev = flush.device
+    p = int(cfg["prefix_lens"][0])
+    pool = torch.from_numpy(np.ascontiguousarray(cfg["pool"]).view(np.int16)).view(torch.bfloat16).to(dev)
+    idx = torch.from_numpy(np.ascontiguousarray(cfg["kv_indices"][:p], dtype=np.int32)).to(dev)
+    out = {}
+    for name, lds in (("register", False), ("lds", True)):
+        out[name] = {}
+        for g in grids:
+            sink = torch.empty(g * 256, dtype=torch.int32, device=dev)
+            for _ in range(2):
+                flush.add_(1.0)
+                mv.probe_gather(pool, idx, lds, g, sink)
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+            for a, b in ev:
+                flush.add_(1.0)
+                a.record()
+                mv.probe_gather(pool, idx, lds, g, sink)
+                b.record()
+            torch.cuda.synchronize()
+            ms = statistics.median(a.elapsed_time(b) for a, b in ev)
+            out[name][str(g)] = round(p * KV_ROW_BYTES / (ms * 1e-3) / 1e9, 1)
+    return out
+
+
+def bench_gather(args) -> int:
+    import torch
+
+    from workloads import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = synth.make_config(3)
+    flush = torch.zeros(1 << 28, dtype=torch.float32, device=dev)
+    copy_gbs = stream_bandwidth(flush)
+    t0 = time.perf_counter()
+    rates = gather_probe(cfg, flush, reps=args.steps)
+    wall = time.perf_counter() - t0
+    best = max(rates["register"].values())
+    p = int(cfg["prefix_lens"][0])
+    line = {
+        "metric": GATHER_METRIC, "value": best, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": 2,
+        "ms_per_step": round(p * KV_ROW_BYTES / (best * 1e9) * 1e3, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "u8", "data": "synthetic",
+        "config": {"workload": "gather_p185000_pool262144", "rows": p, "row_bytes": KV_ROW_BYTES,
+                   "pool_slots": cfg["slots"], "indices": "the 185k workload's scattered prefix slots",
+                   "threads_per_row": 8, "loads_in_flight_per_thread": 36},
+        "rates_gbs": rates, "hbm_stream_gbs": round(copy_gbs, 1),
+        "pct_hbm_measured": round(100 * best / copy_gbs, 2),
+        "wall_s_timed_loop": round(wall, 3),
+        "roofline": {"bound": "hbm", "achieved": best, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(best / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "k_probe_gather<register>"},
+    }
+    if not args.no_cpu:
+        t0 = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t0 < 3.0:
+            cfg["pool"][cfg["kv_indices"][:p]].sum(dtype=np.uint64)
+            reps += 1
+        secs = (time.perf_counter() - t0) / reps
+        line["cpu_baseline"] = {"value": round(p * KV_ROW_BYTES / secs / 1e9, 3), "unit": "GB/s", "cores": 1,
+                                "kind": "numpy gather", "sample": f"pool[indices] of the same rows, {reps} times",
+                                "cpu_model": lscpu_model()}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=3, help="workload index (workloads.synth.CONFIGS)")
     ap.add_argument("--variant", default=None, help="workload variant, e.g. contiguous or sorted")
     ap.add_argument("--warm", action="store_true", help="do not flush caches between calls")
@@ -320,8 +404,10 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--split", type=int, default=0, help="fixed split length (0 = automatic)")
-    ap.add_argument("--op", choices=("verify", "relocate", "accept"), default="verify")
+    ap.add_argument("--op", choices=("verify", "relocate", "accept", "gather"), default="verify")
     ap.add_argument("--page", type=int, default=0, help="prefix page size (block table of page ids); 0 = per token")
+    ap.add_argument("--no-per-config", action="store_true",
+                    help="time only the chosen workload (by default the 185k run also times every other one)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
@@ -330,6 +416,8 @@ def main() -> int:
         return bench_relocate(args)
     if args.op == "accept":
         return bench_accept(args)
+    if args.op == "gather":
+        return bench_gather(args)
 
     import torch
 
@@ -340,105 +428,20 @@ def main() -> int:
         raise SystemExit(f"{mv.LIB_PATH} not built: run `python -m mla_tree_verify_mlaverify_amd.build`")
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    cfg = synth.make_config(args.config, variant=args.variant)
-    workload = synth.CONFIGS[args.config]["name"] + (f"+{args.variant}" if args.variant else "")
-    if args.page > 1:  # the same shapes with paged prefixes (pages drawn at random, tree slots apart)
-        cfg = synth.paged_config(args.config, batch=cfg["batch"], prefix=[int(p) for p in cfg["prefix_lens"]],
-                                 tree_nodes=cfg["tree_nodes"], heads=cfg["heads"], slots=cfg["slots"], page=args.page)
-        workload += f"+paged{args.page}"
+    flush = torch.zeros(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB, read and written before each call
+    copy_gbs = stream_bandwidth(flush)
+
+    cfg, workload = verify_workload(args.config, args.variant, args.page)
+    res = time_verify(cfg, args, flush, args.steps, args.warmup, graph=args.graph, split=args.split, page=args.page)
     counts = algorithmic_counts(cfg)
-
-    def bf16(a):
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
-
-    def i32(a):
-        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
-
-    q, pool = bf16(cfg["q"]), bf16(cfg["pool"])
-    kv_idx, plens, par = i32(cfg["kv_indices"]), i32(cfg["prefix_lens"]), i32(cfg["tree_parent"])
-    v = mv.Verifier(num_heads=cfg["heads"], max_batch=cfg["batch"], max_tree_nodes=cfg["tree_nodes"],
-                    max_prefix_len=int(cfg["prefix_lens"].max()), pool_slots=cfg["slots"],
-                    sm_scale=cfg["sm_scale"], split_tokens=args.split, page_size=args.page, device=dev)
-    b, t, h = cfg["batch"], cfg["tree_nodes"], cfg["heads"]
-    out = torch.empty((b * t, h, 512), dtype=torch.bfloat16, device=dev)
-    lse = torch.empty((b * t, h), dtype=torch.float32, device=dev)
-    flush = torch.zeros(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
-    stream = torch.cuda.current_stream()
-
-    def step():
-        v.run(q, pool, kv_idx, plens, par, out=out, lse=lse, stream=stream)
-
-    for _ in range(args.warmup):
-        if not args.warm:
-            flush.add_(1.0)
-        step()
-    torch.cuda.synchronize()
-    call = step
-    if args.graph:  # the same call, captured once on a side stream and replayed on this one
-        gs = torch.cuda.Stream(device=dev)
-        gs.wait_stream(stream)
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=gs):
-            v.run(q, pool, kv_idx, plens, par, out=out, lse=lse, stream=gs)
-        torch.cuda.synchronize()
-        call = graph.replay
-        for _ in range(args.warmup):
-            if not args.warm:
-                flush.add_(1.0)
-            call()
-        torch.cuda.synchronize()
-
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    # Whole calls, timed on their own: the library's per-kernel events (below) would add
-    # their own markers between the two launches.
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    for k in range(args.steps):
-        if not args.warm:
-            flush.add_(1.0)
-        starts[k].record(stream)
-        call()
-        ends[k].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    call_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    # The same calls again with the library's HIP events around each of its kernels.
-    v.profile_begin(args.steps)
-    for k in range(args.steps):
-        if not args.warm:
-            flush.add_(1.0)
-        step()
-    torch.cuda.synchronize()
-    kernel_ms = v.profile_end()
-    errs = v.read_device_errors()
-    assert errs == 0, errs
-
-    med_ms = statistics.median(call_ms)
-    p10, p90 = np.percentile(call_ms, 10), np.percentile(call_ms, 90)
-    part_ms = [k[0] for k in kernel_ms]
-    part_avg = sum(part_ms) / len(part_ms)
-    kv_gbs = counts["kv_bytes"] / (med_ms * 1e-3) / 1e9
-    tflops = counts["flops"] / (med_ms * 1e-3) / 1e12
-    part_tflops = counts["flops"] / (part_avg * 1e-3) / 1e12
-    t_hbm = counts["total_bytes"] / (HBM_PEAK_GBS * 1e9)
-    t_mfma = counts["flops"] / (BF16_MFMA_PEAK_TFLOPS * 1e12)
-    bound = "mfma" if t_mfma >= t_hbm else "hbm"
-    if bound == "mfma":
-        roof = {"bound": "mfma", "achieved": round(part_tflops, 2), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(part_tflops / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None}
-    else:
-        part_gbs = counts["total_bytes"] / (part_avg * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(part_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(part_gbs / HBM_PEAK_GBS, 4), "traffic": None}
+    summ = verify_summary(cfg, counts, res, copy_gbs)
+    med_ms = res["call_ms_median"]
+    roof = summ["roofline"]
     roof["traffic"] = (stored_traffic(synth.CONFIGS[args.config]["name"])
                        if not (args.variant or args.split or args.warm or args.page > 1) else None)
-    roof["kernel"] = "k_partial"
-    roof["kernel_avg_us"] = round(part_avg * 1e3, 2)
-
     line = {
         "metric": METRIC,
-        "value": round(kv_gbs, 2),
+        "value": summ["kv_gbs"],
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -450,26 +453,190 @@ def main() -> int:
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": workload,
-                   "batch": b, "tree_nodes": t, "heads": h,
+                   "batch": cfg["batch"], "tree_nodes": cfg["tree_nodes"], "heads": cfg["heads"],
                    "prefix_lens": [int(x) for x in cfg["prefix_lens"]], "pool_slots": cfg["slots"],
                    "split": args.split or "auto", "cache": "warm" if args.warm else "flushed 1 GiB before each call",
                    "call": "HIP graph replay" if args.graph else "eager"},
-        "us_per_call": {"median": round(med_ms * 1e3, 2), "p10": round(float(p10) * 1e3, 2),
-                        "p90": round(float(p90) * 1e3, 2)},
-        "pct_hbm_peak": round(100 * kv_gbs / HBM_PEAK_GBS, 2),
-        "tflops": round(tflops, 2),
-        "pct_mfma_peak": round(100 * tflops / BF16_MFMA_PEAK_TFLOPS, 2),
-        "roofline_frac_call": round(max(t_hbm, t_mfma) / (med_ms * 1e-3), 4),
-        "kernels_us": {"partial": round(part_avg * 1e3, 2),
-                       "merge": round(1e3 * sum(k[1] for k in kernel_ms) / len(kernel_ms), 2)},
-        "wall_s_timed_loop": round(wall, 4),
-        "roofline": roof,
-        "plan": {k: v.read_plan()[k] for k in ("split_len", "total_units", "n_mtiles")},
+        "wall_s_timed_loop": res["wall_s"],
+        "hbm_stream_gbs": round(copy_gbs, 1),
     }
+    line.update({k: summ[k] for k in ("us_per_call", "kernels_us", "pct_hbm_peak", "pct_hbm_measured", "tflops",
+                                      "pct_mfma_peak", "roofline_frac_call", "sclk_mhz", "plan")})
+    line["roofline"] = roof
+    del res
+    if not args.no_per_config and args.config == 3 and not (args.variant or args.page > 1 or args.split):
+        # the other seeded workloads, timed in the same run with the same protocol (fewer calls)
+        per = {}
+        steps = max(10, args.steps // 2)
+        for i, var in PER_CONFIG:
+            c, name = verify_workload(i, var, 0)
+            r = time_verify(c, args, flush, steps, min(args.warmup, 3), graph=False, split=0, page=0)
+            per[name] = verify_summary(c, algorithmic_counts(c), r, copy_gbs)
+            per[name]["steps"] = steps
+            del r, c
+            torch.cuda.empty_cache()
+        line["per_config"] = per
+        # the scattered-read ceiling of the two load paths on the headline's own rows
+        line["gather_probe_gbs"] = gather_probe(cfg, flush, grids=(512,))
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(cfg, counts, args.cpu_budget)
     print(json.dumps(line), flush=True)
     return 0
+
+
+# The seeded workloads other than the 185k headline, each timed once per default run: the
+# 4k and 65k prefixes (the 65k one also with its indices sorted, and as one contiguous run),
+# the batch of 8, and the two HBM-bound small-tree shapes.
+PER_CONFIG = [(1, None), (2, None), (2, "sorted"), (2, "contiguous"), (4, None), (5, None), (6, None)]
+
+
+def verify_workload(i: int, variant, page: int):
+    from workloads import synth
+
+    cfg = synth.make_config(i, variant=variant)
+    name = synth.CONFIGS[i]["name"] + (f"+{variant}" if variant else "")
+    if page > 1:  # the same shapes with paged prefixes (pages drawn at random, tree slots apart)
+        cfg = synth.paged_config(i, batch=cfg["batch"], prefix=[int(p) for p in cfg["prefix_lens"]],
+                                 tree_nodes=cfg["tree_nodes"], heads=cfg["heads"], slots=cfg["slots"], page=page)
+        name += f"+paged{page}"
+    return cfg, name
+
+
+def stream_bandwidth(flush) -> float:
+    """Measured HBM rate of a plain streaming kernel: the 1 GiB read-modify-write used as the cache
+    flush (2 GiB of traffic per launch), median of 10 launches, GB/s."""
+    import torch
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(12)]
+    for a, b in ev:
+        a.record()
+        flush.add_(1.0)
+        b.record()
+    torch.cuda.synchronize()
+    ms = statistics.median(a.elapsed_time(b) for a, b in ev[2:])
+    return 2 * flush.numel() * 4 / (ms * 1e-3) / 1e9
+
+
+def time_verify(cfg: dict, args, flush, steps: int, warmup: int, *, graph: bool, split: int, page: int) -> dict:
+    """Upload one workload, then time `steps` whole calls (one HIP event pair around each, caches
+    flushed before each unless --warm) and `steps` more with the library's events around each
+    kernel.  Returns per-call milliseconds, per-kernel milliseconds and the plan."""
+    import torch
+
+    import mla_tree_verify_mlaverify_amd as mv
+
+    dev = flush.device
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def i32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+
+    q, pool = bf16(cfg["q"]), bf16(cfg["pool"])
+    kv_idx, plens, par = i32(cfg["kv_indices"]), i32(cfg["prefix_lens"]), i32(cfg["tree_parent"])
+    v = mv.Verifier(num_heads=cfg["heads"], max_batch=cfg["batch"], max_tree_nodes=cfg["tree_nodes"],
+                    max_prefix_len=int(cfg["prefix_lens"].max()), pool_slots=cfg["slots"],
+                    sm_scale=cfg["sm_scale"], split_tokens=split, page_size=page, device=dev)
+    b, t, h = cfg["batch"], cfg["tree_nodes"], cfg["heads"]
+    out = torch.empty((b * t, h, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((b * t, h), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        v.run(q, pool, kv_idx, plens, par, out=out, lse=lse, stream=stream)
+
+    for _ in range(warmup):
+        if not args.warm:
+            flush.add_(1.0)
+        step()
+    torch.cuda.synchronize()
+    call = step
+    if graph:  # the same call, captured once on a side stream and replayed on this one
+        gs = torch.cuda.Stream(device=dev)
+        gs.wait_stream(stream)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=gs):
+            v.run(q, pool, kv_idx, plens, par, out=out, lse=lse, stream=gs)
+        torch.cuda.synchronize()
+        call = g.replay
+        for _ in range(warmup):
+            if not args.warm:
+                flush.add_(1.0)
+            call()
+        torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    # Whole calls, timed on their own: the library's per-kernel events (below) would add
+    # their own markers between the two launches.
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for k in range(steps):
+        if not args.warm:
+            flush.add_(1.0)
+        starts[k].record(stream)
+        call()
+        ends[k].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    call_ms = [s_.elapsed_time(e) for s_, e in zip(starts, ends)]
+    # The same calls again with the library's HIP events around each of its kernels.
+    v.profile_begin(steps)
+    for _ in range(steps):
+        if not args.warm:
+            flush.add_(1.0)
+        step()
+    torch.cuda.synchronize()
+    kernel_ms = v.profile_end()
+    errs = v.read_device_errors()
+    assert errs == 0, errs
+    plan = v.read_plan()
+    return dict(call_ms=call_ms, call_ms_median=statistics.median(call_ms), kernel_ms=kernel_ms, plan=plan,
+                wall_s=round(wall, 4))
+
+
+def verify_summary(cfg: dict, counts: dict, res: dict, copy_gbs: float) -> dict:
+    """The metric's figures for one timed workload: µs per call, KV GB/s and %HBM (of the nominal
+    peak and of the measured stream rate), %MFMA, and the partial kernel's roofline."""
+    call_ms = res["call_ms"]
+    med_ms = res["call_ms_median"]
+    part_ms = [k[0] for k in res["kernel_ms"]]
+    merge_ms = [k[1] for k in res["kernel_ms"]]
+    part_avg = sum(part_ms) / len(part_ms)
+    kv_gbs = counts["kv_bytes"] / (med_ms * 1e-3) / 1e9
+    tflops = counts["flops"] / (med_ms * 1e-3) / 1e12
+    t_hbm = counts["total_bytes"] / (HBM_PEAK_GBS * 1e9)
+    t_mfma = counts["flops"] / (BF16_MFMA_PEAK_TFLOPS * 1e12)
+    if t_mfma >= t_hbm:
+        ach = counts["flops"] / (part_avg * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None}
+    else:
+        ach = counts["total_bytes"] / (part_avg * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
+    roof["kernel"] = "k_partial"
+    roof["kernel_avg_us"] = round(part_avg * 1e3, 2)
+    plan = res["plan"]
+    s = plan["split_len"]
+    prefix_units = sum(min(r["units"], -(-r["prefix_len"] // s)) for r in plan["requests"])
+    return {
+        "us_per_call": {"median": round(med_ms * 1e3, 2), "p10": round(float(np.percentile(call_ms, 10)) * 1e3, 2),
+                        "p90": round(float(np.percentile(call_ms, 90)) * 1e3, 2)},
+        "kernels_us": {"partial": round(part_avg * 1e3, 2), "merge": round(1e3 * sum(merge_ms) / len(merge_ms), 2),
+                       "call_minus_partial": round(med_ms * 1e3 - part_avg * 1e3, 2)},
+        "kv_gbs": round(kv_gbs, 2),
+        "pct_hbm_peak": round(100 * kv_gbs / HBM_PEAK_GBS, 2),
+        "pct_hbm_measured": round(100 * kv_gbs / copy_gbs, 2),
+        "tflops": round(tflops, 2),
+        "pct_mfma_peak": round(100 * tflops / BF16_MFMA_PEAK_TFLOPS, 2),
+        "roofline_frac_call": round(max(t_hbm, t_mfma) / (med_ms * 1e-3), 4),
+        "sclk_mhz": plan.get("sclk_mhz"),
+        "roofline": roof,
+        "plan": {"split_len": s, "total_units": plan["total_units"], "n_mtiles": plan["n_mtiles"],
+                 "fast_units": plan["fast_units"], "prefix_units": prefix_units,
+                 "fast_hit_rate": round(plan["fast_units"] / prefix_units, 4) if prefix_units else None},
+    }
 
 
 if __name__ == "__main__":

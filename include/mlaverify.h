@@ -68,6 +68,8 @@ extern "C" {
                                              since their index segments can no longer be located */
 #define MLAVERIFY_DEVERR_RELOCATE_CONFLICT 0x8u /* mlaverify_relocate refused: a destination run leaves
                                                    the pool, overlaps another one or holds a slot in use */
+#define MLAVERIFY_DEVERR_BAD_TREE_LEN 0x10u /* mlaverify_run_ragged: a tree_lens entry outside [1, max_T];
+                                               that request and every later one are poisoned */
 
 /* Flags for mlaverify_config.flags. */
 #define MLAVERIFY_FLAG_NO_FASTPATH 0x1u   /* always gather row by row (A/B tests of the contiguous path) */
@@ -133,6 +135,28 @@ MLAVERIFY_API int mlaverify_run(mlaverify_t h, int32_t batch, int32_t tree_nodes
                                 const void* q, const void* kv_pool, const int32_t* kv_indices,
                                 const int32_t* prefix_lens, const int32_t* tree_parent,
                                 void* out, float* lse, void* stream);
+
+/* The verify pass for a batch whose requests draft trees of different sizes (a budget per
+ * request, as the DDTree verify step of the "Chunk 66.0" summary runs one draft tree per
+ * request; the reading of the layout below is this library's).  Request b has
+ * T_b = tree_lens[b] nodes, 1 <= T_b <= max_T <= max_tree_nodes; max_T (host) sizes the
+ * launch, the kernels size each request's work by its own T_b, so a small tree costs no
+ * padded rows.  Rows are packed request after request: node i of request b is row n_b + i
+ * with n_b = T_0 + ... + T_{b-1}.  Device arguments (as for mlaverify_run otherwise):
+ *   tree_lens   int32 [batch]
+ *   q           bf16 [sum T_b, H, 576], row (n_b + i)*H + h
+ *   kv_indices  int32 [sum_b (E_b + T_b)]: request b's prefix entries, then its T_b tree slots
+ *   tree_parent int32 [sum T_b]: at n_b + i the parent of node i within its request
+ *               (-1, or an earlier node of the same request)
+ *   out, lse    [sum T_b, H, 512] and [sum T_b, H] (written)
+ * A T_b outside [1, max_T] sets MLAVERIFY_DEVERR_BAD_TREE_LEN and poisons that request and
+ * every later one: their rows' positions depend on it, so none of their rows is written.
+ * With every T_b equal to T the results are those of mlaverify_run, bit for bit.  Never
+ * synchronises, copies to or from the host or allocates: graph-capturable. */
+MLAVERIFY_API int mlaverify_run_ragged(mlaverify_t h, int32_t batch, int32_t max_T, const int32_t* tree_lens,
+                                       const void* q, const void* kv_pool, const int32_t* kv_indices,
+                                       const int32_t* prefix_lens, const int32_t* tree_parent, void* out,
+                                       float* lse, void* stream);
 
 /* Bytes of the static device workspace behind mlaverify_run_static (48 MiB per GPU). */
 #define MLAVERIFY_STATIC_SCRATCH_BYTES ((size_t)48 << 20)
@@ -223,13 +247,29 @@ MLAVERIFY_API int mlaverify_accept(mlaverify_t h, int32_t batch, int32_t tree_no
 MLAVERIFY_API int mlaverify_tree_masks(const int32_t* tree_parent, int32_t batch, int32_t tree_nodes,
                                        uint64_t* masks, uint32_t* err, void* stream);
 
+/* Measurement probe, not part of the verify pass: enqueues one launch that reads the pool
+ * rows kv_pool[indices[r]] (columns 0..575, 1,152 bytes each) for r < n_rows, the scattered
+ * page_size=1 access pattern whose 128-bit loads the "Chunk 66.1" summary credits, through
+ * one of the two 16-byte load paths the verify kernel can use: lds_path = 0 loads into
+ * registers (non-temporal global_load_dwordx4), lds_path != 0 loads straight into LDS
+ * (global_load_lds_dwordx4).  grid workgroups of 256 threads (1 .. 2^20); each reads tiles
+ * of 32 rows, four tiles in flight.  Entries outside [0, pool_slots) read row 0.
+ * sink: device uint32 [grid * 256], written with a fold of the data read (its value is of no
+ * use; it keeps the loads live).  Device pointers: kv_pool (16-byte aligned), indices, sink.
+ * Enqueued on `stream`; no synchronisation or allocation. */
+MLAVERIFY_API int mlaverify_probe_gather(const void* kv_pool, int64_t kv_row_stride, int64_t pool_slots,
+                                         const int32_t* indices, int32_t n_rows, int32_t lds_path, int32_t grid,
+                                         uint32_t* sink, void* stream);
+
 /* Copies the work partition of the most recent run into host memory (synchronises
  * `stream`; for tests and reports, not for graphs).  Writes up to `capacity`
- * int32 values: [split_len, total_units, n_mtiles, fast_units, then per request b:
- * key_offset_b, prefix_len_b, first_unit_b, units_b, prefix_error_bits_b], where
- * fast_units counts the split units whose prefix slots formed one contiguous run and
- * were read without the index table (the contiguous-run fast path; a unit with no
- * prefix keys never counts).  Parent and index errors are reported by
+ * int32 values: [split_len, total_units, n_mtiles, fast_units, sclk_khz, then per
+ * request b: key_offset_b, prefix_len_b, first_unit_b, units_b, prefix_error_bits_b],
+ * where fast_units counts the split units whose prefix slots formed one contiguous run
+ * and were read without the index table (the contiguous-run fast path; a unit with no
+ * prefix keys never counts), and sclk_khz is the shader clock over the run of the
+ * partial kernel's first workgroup (its cycle counter against the device's wall clock;
+ * 0 if it was not sampled).  Parent and index errors are reported by
  * mlaverify_read_device_errors only.
  * Returns the number of values available (which may exceed capacity) or a
  * negative status. */

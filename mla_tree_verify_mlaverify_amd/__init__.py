@@ -9,6 +9,7 @@ from .binding import (  # noqa: F401
     DEVERR_BAD_PARENT,
     DEVERR_BAD_PREFIX,
     DEVERR_RELOCATE_CONFLICT,
+    DEVERR_BAD_TREE_LEN,
     FLAG_NO_FASTPATH,
     LATENT_DIM,
     LIB_PATH,

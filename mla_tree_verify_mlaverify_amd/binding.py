@@ -33,6 +33,7 @@ DEVERR_BAD_PARENT = 0x1
 DEVERR_BAD_INDEX = 0x2
 DEVERR_BAD_PREFIX = 0x4
 DEVERR_RELOCATE_CONFLICT = 0x8
+DEVERR_BAD_TREE_LEN = 0x10
 
 FLAG_NO_FASTPATH = 0x1
 
@@ -43,9 +44,11 @@ EXPORTED = (
     "mlaverify_create",
     "mlaverify_run",
     "mlaverify_run_static",
+    "mlaverify_run_ragged",
     "mlaverify_relocate",
     "mlaverify_accept",
     "mlaverify_tree_masks",
+    "mlaverify_probe_gather",
     "mlaverify_read_plan",
     "mlaverify_read_device_errors",
     "mlaverify_profile_begin",
@@ -101,12 +104,17 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.mlaverify_run.restype = ctypes.c_int
     lib.mlaverify_run_static.argtypes = [cfg_p, c_int32, c_int32] + [c_void_p] * 8
     lib.mlaverify_run_static.restype = ctypes.c_int
+    lib.mlaverify_run_ragged.argtypes = [c_void_p, c_int32, c_int32] + [c_void_p] * 9
+    lib.mlaverify_run_ragged.restype = ctypes.c_int
     lib.mlaverify_relocate.argtypes = [c_void_p, c_int32, c_int32] + [c_void_p] * 5
     lib.mlaverify_relocate.restype = ctypes.c_int
     lib.mlaverify_accept.argtypes = [c_void_p, c_int32, c_int32, c_int32] + [c_void_p] * 7
     lib.mlaverify_accept.restype = ctypes.c_int
     lib.mlaverify_tree_masks.argtypes = [c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p]
     lib.mlaverify_tree_masks.restype = ctypes.c_int
+    lib.mlaverify_probe_gather.argtypes = [c_void_p, ctypes.c_int64, ctypes.c_int64, c_void_p, c_int32, c_int32, c_int32,
+                                           c_void_p, c_void_p]
+    lib.mlaverify_probe_gather.restype = ctypes.c_int
     lib.mlaverify_read_plan.argtypes = [c_void_p, c_int32, c_void_p, ctypes.POINTER(c_int32), c_int32]
     lib.mlaverify_read_plan.restype = ctypes.c_int
     lib.mlaverify_read_device_errors.argtypes = [c_void_p, c_void_p, ctypes.POINTER(ctypes.c_uint32)]
@@ -234,6 +242,44 @@ class Verifier:
         self.last_batch = b
         return out, lse
 
+    def run_ragged(self, q, kv_pool, kv_indices, prefix_lens, tree_lens, tree_parent, max_tree_nodes: int,
+                   out=None, lse=None, stream=None):
+        """Verify attention for requests with trees of different sizes (mlaverify_run_ragged):
+        tree_lens int32 [B] on the device, rows packed request after request; max_tree_nodes is
+        the largest tree length of the call (a host int).  Returns (out [sum T_b, H, 512],
+        lse [sum T_b, H]); the caller gives the row count through q's first dimension."""
+        h = self.num_heads
+        dev = self.device
+        _check(tree_lens, "tree_lens", torch.int32, None, dev)
+        if tree_lens.dim() != 1:
+            raise ValueError("tree_lens must be 1-D")
+        b = tree_lens.shape[0]
+        if q.dim() != 3:
+            raise ValueError("q must be [sum T_b, H, 576]")
+        rows = q.shape[0]
+        _check(q, "q", torch.bfloat16, (rows, h, LATENT_DIM), dev)
+        _check(tree_parent, "tree_parent", torch.int32, (rows,), dev)
+        _check(prefix_lens, "prefix_lens", torch.int32, (b,), dev)
+        _check(kv_indices, "kv_indices", torch.int32, None, dev)
+        if kv_indices.dim() != 1:
+            raise ValueError("kv_indices must be 1-D")
+        _check(kv_pool, "kv_pool", torch.bfloat16, (self.cfg.pool_slots, self.cfg.kv_row_stride), dev)
+        if out is None:
+            out = torch.empty((rows, h, V_DIM), dtype=torch.bfloat16, device=dev)
+        if lse is None:
+            lse = torch.empty((rows, h), dtype=torch.float32, device=dev)
+        _check(out, "out", torch.bfloat16, (rows, h, V_DIM), dev)
+        _check(lse, "lse", torch.float32, (rows, h), dev)
+        with torch.cuda.device(dev):
+            rc = self.lib.mlaverify_run_ragged(self.handle, b, max_tree_nodes, tree_lens.data_ptr(), q.data_ptr(),
+                                               kv_pool.data_ptr(), kv_indices.data_ptr(), prefix_lens.data_ptr(),
+                                               tree_parent.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                               _stream_handle(stream))
+        if rc != OK:
+            raise MlaVerifyError(rc, "mlaverify_run_ragged")
+        self.last_batch = b
+        return out, lse
+
     def relocate(self, kv_pool, kv_indices, prefix_lens, dst_start, tree_nodes: int, stream=None) -> None:
         """Tier-1 relocation of the batch's prefix rows into the runs starting at dst_start
         (in place on kv_pool and kv_indices; refusals show in read_device_errors)."""
@@ -279,15 +325,16 @@ class Verifier:
     def read_plan(self, batch: int | None = None, stream=None) -> dict:
         """Work partition of the last run (synchronises the stream)."""
         batch = batch or self.last_batch
-        cap = 4 + 5 * batch
+        cap = 5 + 5 * batch
         buf = (ctypes.c_int32 * cap)()
         n = self.lib.mlaverify_read_plan(self.handle, batch, _stream_handle(stream), buf, cap)
         if n < 0:
             raise MlaVerifyError(n, "mlaverify_read_plan")
         vals = list(buf)
-        reqs = [dict(zip(("key_offset", "prefix_len", "first_unit", "units", "error_bits"), vals[4 + 5 * i:9 + 5 * i]))
+        reqs = [dict(zip(("key_offset", "prefix_len", "first_unit", "units", "error_bits"), vals[5 + 5 * i:10 + 5 * i]))
                 for i in range(batch)]
-        return dict(split_len=vals[0], total_units=vals[1], n_mtiles=vals[2], fast_units=vals[3], requests=reqs)
+        return dict(split_len=vals[0], total_units=vals[1], n_mtiles=vals[2], fast_units=vals[3],
+                    sclk_mhz=round(vals[4] / 1000.0, 1), requests=reqs)
 
     def profile_begin(self, max_runs: int) -> None:
         """Record HIP events around the kernels of the next max_runs runs."""
@@ -312,6 +359,23 @@ class Verifier:
         if rc != OK:
             raise MlaVerifyError(rc, "mlaverify_read_device_errors")
         return flags.value
+
+
+def probe_gather(kv_pool, indices, lds_path: bool, grid: int, sink, pool_slots: int | None = None, stream=None) -> None:
+    """One launch of the scattered-row read probe (mlaverify_probe_gather): reads kv_pool[indices]
+    into registers (lds_path False) or into LDS (True); sink (uint32 [grid * 256]) keeps the loads live."""
+    lib = load_library()
+    dev = kv_pool.device
+    _check(kv_pool, "kv_pool", torch.bfloat16, None, dev)
+    _check(indices, "indices", torch.int32, None, dev)
+    _check(sink, "sink", torch.int32, (grid * 256,), dev)
+    slots, stride = kv_pool.shape
+    with torch.cuda.device(dev):
+        rc = lib.mlaverify_probe_gather(kv_pool.data_ptr(), stride, pool_slots or slots, indices.data_ptr(),
+                                        indices.numel(), 1 if lds_path else 0, grid, sink.data_ptr(),
+                                        _stream_handle(stream))
+    if rc != OK:
+        raise MlaVerifyError(rc, "mlaverify_probe_gather")
 
 
 STATIC_SCRATCH_BYTES = 48 << 20

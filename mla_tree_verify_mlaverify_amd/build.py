@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libmlaverify.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
-SOURCES = ("api.hip", "kernels.hip", "relocate.hip", "accept.hip")
+SOURCES = ("api.hip", "kernels.hip", "relocate.hip", "accept.hip", "probe.hip")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -184,6 +184,8 @@ def audit_mfma_operands(asm: str, wait_states: int = 2) -> list[str]:
         if st.startswith(";;#ASMEND"):
             in_asm = False
             continue
+        if st.startswith(";"):
+            continue  # a comment line (block comments such as "; %bb.3:" included)
         if line and not line[0].isspace() and st.endswith(":"):
             if st.startswith("."):
                 recent.append(("<label>", ""))  # a branch target

@@ -135,9 +135,9 @@ size_t run_offsets(const mlaverify_config& c, int batch, int T, RunOffsets* o) {
 
 // Enqueues the two kernels of one verify pass (plan + partials, then the merge) over the
 // workspace areas w; records the profiling events ev[0..2] around them when ev is given.
-int enqueue_run(const mlaverify_config& c, const RunAreas& w, int batch, int T, const void* q, const void* kv_pool,
-                const int32_t* kv_indices, const int32_t* prefix_lens, const int32_t* tree_parent, void* out,
-                float* lse, hipStream_t s, hipEvent_t* ev) {
+int enqueue_run(const mlaverify_config& c, const RunAreas& w, int batch, int T, const int32_t* tree_lens,
+                const void* q, const void* kv_pool, const int32_t* kv_indices, const int32_t* prefix_lens,
+                const int32_t* tree_parent, void* out, float* lse, hipStream_t s, hipEvent_t* ev) {
   const int n_mt = mtiles_for(c.num_heads, T);
   const int units_grid = units_for(c, batch, T);
   const int M = c.num_heads * T;
@@ -148,6 +148,7 @@ int enqueue_run(const mlaverify_config& c, const RunAreas& w, int batch, int T, 
   ka.kv_indices = kv_indices;
   ka.prefix_lens = prefix_lens;
   ka.tree_parent = tree_parent;
+  ka.tree_lens = tree_lens;
   ka.hdr = w.hdr;
   ka.req = w.req;
   ka.part_o = w.part_o;
@@ -179,6 +180,7 @@ int enqueue_run(const mlaverify_config& c, const RunAreas& w, int batch, int T, 
   ma.out = static_cast<uint16_t*>(out);
   ma.lse = lse;
   ma.batch = batch;
+  ma.H = c.num_heads;
   ma.M = M;
   ma.units_cap = units_grid;
 
@@ -310,8 +312,29 @@ int mlaverify_run(mlaverify_t hd, int32_t batch, int32_t T, const void* q, const
                       reinterpret_cast<uint16_t*>(hd->ws + L.part_o)};
   hipEvent_t* ev = nullptr;
   if (hd->prof_runs < hd->prof_max) ev = &hd->prof_events[3 * hd->prof_runs++];
-  const int rc = enqueue_run(c, w, batch, T, q, kv_pool, kv_indices, prefix_lens, tree_parent, out, lse,
+  const int rc = enqueue_run(c, w, batch, T, nullptr, q, kv_pool, kv_indices, prefix_lens, tree_parent, out, lse,
                              static_cast<hipStream_t>(stream), ev);
+  if (rc == MLAVERIFY_OK) hd->last_batch = batch;
+  return rc;
+}
+
+int mlaverify_run_ragged(mlaverify_t hd, int32_t batch, int32_t max_T, const int32_t* tree_lens, const void* q,
+                         const void* kv_pool, const int32_t* kv_indices, const int32_t* prefix_lens,
+                         const int32_t* tree_parent, void* out, float* lse, void* stream) {
+  if (!hd) return MLAVERIFY_ERR_INVALID_ARG;
+  if (!on_handle_device(hd)) return MLAVERIFY_ERR_INVALID_ARG;
+  const mlaverify_config& c = hd->cfg;
+  const int v = check_run_args(c, batch, max_T, q, kv_pool, kv_indices, prefix_lens, tree_parent, out, lse);
+  if (v != MLAVERIFY_OK) return v;
+  if (!tree_lens || !aligned(tree_lens, 4)) return MLAVERIFY_ERR_INVALID_ARG;
+  const Layout& L = hd->L;
+  const RunAreas w = {reinterpret_cast<PlanHeader*>(hd->ws + L.hdr), reinterpret_cast<ReqPlan*>(hd->ws + L.req),
+                      reinterpret_cast<int32_t*>(hd->ws + L.unit_tab), reinterpret_cast<float*>(hd->ws + L.part_lse),
+                      reinterpret_cast<uint16_t*>(hd->ws + L.part_o)};
+  hipEvent_t* ev = nullptr;
+  if (hd->prof_runs < hd->prof_max) ev = &hd->prof_events[3 * hd->prof_runs++];
+  const int rc = enqueue_run(c, w, batch, max_T, tree_lens, q, kv_pool, kv_indices, prefix_lens, tree_parent, out,
+                             lse, static_cast<hipStream_t>(stream), ev);
   if (rc == MLAVERIFY_OK) hd->last_batch = batch;
   return rc;
 }
@@ -331,7 +354,7 @@ int mlaverify_run_static(const mlaverify_config* c, int32_t batch, int32_t T, co
   const RunAreas w = {reinterpret_cast<PlanHeader*>(base + o.hdr), reinterpret_cast<ReqPlan*>(base + o.req),
                       reinterpret_cast<int32_t*>(base + o.unit_tab), reinterpret_cast<float*>(base + o.part_lse),
                       reinterpret_cast<uint16_t*>(base + o.part_o)};
-  return enqueue_run(*c, w, batch, T, q, kv_pool, kv_indices, prefix_lens, tree_parent, out, lse,
+  return enqueue_run(*c, w, batch, T, nullptr, q, kv_pool, kv_indices, prefix_lens, tree_parent, out, lse,
                      static_cast<hipStream_t>(stream), nullptr);
 }
 
@@ -407,11 +430,23 @@ int mlaverify_tree_masks(const int32_t* tree_parent, int32_t batch, int32_t T, u
   return MLAVERIFY_OK;
 }
 
+int mlaverify_probe_gather(const void* kv_pool, int64_t kv_row_stride, int64_t pool_slots, const int32_t* indices,
+                           int32_t n_rows, int32_t lds_path, int32_t grid, uint32_t* sink, void* stream) {
+  if (!kv_pool || !indices || !sink || n_rows < 1 || grid < 1 || grid > (1 << 20)) return MLAVERIFY_ERR_INVALID_ARG;
+  if (kv_row_stride < kLatent || kv_row_stride % 8 != 0 || pool_slots < 1) return MLAVERIFY_ERR_INVALID_ARG;
+  if (!aligned(kv_pool, 16) || !aligned(indices, 4) || !aligned(sink, 4)) return MLAVERIFY_ERR_INVALID_ARG;
+  if (launch_probe_gather(kv_pool, kv_row_stride * 2, pool_slots, indices, n_rows, lds_path ? 1 : 0, grid, sink,
+                          static_cast<hipStream_t>(stream)) != hipSuccess)
+    return MLAVERIFY_ERR_HIP;
+  return MLAVERIFY_OK;
+}
+
 int mlaverify_read_plan(mlaverify_t hd, int32_t batch, void* stream, int32_t* host_out, int32_t capacity) {
   if (!hd || batch < 1 || batch > hd->cfg.max_batch || (capacity > 0 && !host_out) || capacity < 0)
     return MLAVERIFY_ERR_INVALID_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int needed = 4 + 5 * batch;
+  constexpr int kPlanHead = 5;
+  const int needed = kPlanHead + 5 * batch;
   PlanHeader hdr;
   std::vector<ReqPlan> req;
   std::vector<int32_t> fast;
@@ -430,12 +465,18 @@ int mlaverify_read_plan(mlaverify_t hd, int32_t batch, void* stream, int32_t* ho
   if (!ok) return MLAVERIFY_ERR_HIP;
   int32_t fast_units = 0;
   for (int u = 0; u < hdr.total_units && u < (int)fast.size(); u++) fast_units += fast[u] != 0;
-  int32_t vals[4] = {hdr.split_len, hdr.total_units, hdr.n_mtiles, fast_units};
-  for (int i = 0; i < 4 && i < capacity; i++) host_out[i] = vals[i];
+  // shader clock of the partial kernel's workgroup 0, from its cycle and wall-clock samples
+  int wall_khz = 0;
+  int32_t sclk_khz = 0;
+  if (hipDeviceGetAttribute(&wall_khz, hipDeviceAttributeWallClockRate, hd->device) == hipSuccess && wall_khz > 0 &&
+      hdr.clk_ticks > 0)
+    sclk_khz = (int32_t)((double)hdr.clk_cycles * wall_khz / hdr.clk_ticks);
+  int32_t vals[kPlanHead] = {hdr.split_len, hdr.total_units, hdr.n_mtiles, fast_units, sclk_khz};
+  for (int i = 0; i < kPlanHead && i < capacity; i++) host_out[i] = vals[i];
   for (int b = 0; b < batch; b++) {
     const int32_t rv[5] = {req[b].key_off, req[b].prefix_len, req[b].first_unit, req[b].units, (int32_t)req[b].err};
     for (int k = 0; k < 5; k++) {
-      const int pos = 4 + 5 * b + k;
+      const int pos = kPlanHead + 5 * b + k;
       if (pos < capacity) host_out[pos] = rv[k];
     }
   }

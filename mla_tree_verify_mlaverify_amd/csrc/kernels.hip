@@ -110,16 +110,18 @@ __device__ __forceinline__ int swz(int key) {
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 // 16-byte global -> LDS load (gfx950 global_load_lds_dwordx4): lane i's 16 bytes land at
-// LDS address m0 + 16 i.  Piece J of a row goes to lds_base + 4096 J (M0 is set with one
-// scalar add); the caller passes the piece's global address.  Issued through asm so that the
-// compiler does not make every later LDS read wait for it; completion is awaited explicitly
-// (vmcnt(0) + barrier) before the tile is read.  The s_nop is the wait state between an M0
-// write and its LDS-DMA use.  M0 is a reserved register that a clobber list cannot protect;
-// the build instead checks that no compiler-generated instruction uses it.
+// LDS address m0 + offset + 16 i, read from the lane's address + offset.  Piece J of a row is
+// the row's 16-byte chunk J * 8 + (lane's chunk) and goes to lds_base + 4096 J: the caller
+// passes the row's address, the instruction offset adds 128 J to both addresses, and M0
+// (one scalar add) takes the rest of the LDS step, 4096 J - 128 J.  Issued through asm so
+// that the compiler does not make every later LDS read wait for it; completion is awaited
+// explicitly (vmcnt(0) + barrier) before the tile is read.  The s_nop is the wait state
+// between an M0 write and its LDS-DMA use.  M0 is a reserved register that a clobber list
+// cannot protect; the build instead checks that no compiler-generated instruction uses it.
 template <int J>
 __device__ __forceinline__ void lds_dma16(const char* gaddr, uint32_t lds_base) {
-  asm volatile("s_add_u32 m0, %1, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               ::"v"(gaddr), "s"(lds_base), "n"(J * 4096));
+  asm volatile("s_add_u32 m0, %1, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off offset:%3"
+               ::"v"(gaddr), "s"(lds_base), "n"(J * (4096 - 128)), "n"(J * 128));
 }
 
 // Score MFMAs (bf16 32x32x16) are compiler builtins with VGPR accumulators (the library is
@@ -263,20 +265,25 @@ __device__ int wg_exclusive_scan(int v, int* s_tmp, int& total) {
   return base + x - v;
 }
 
-// Work partition (row a.2), computed by every workgroup from the prefix lengths:
-//   * prefix lengths outside [0, max_prefix] are errors; such a request and every later
-//     one are poisoned (their index segments can no longer be located) and get no keys;
-//   * key_off_b = exclusive scan of (E_b + T), where E_b = ceil(P_b / page) is the number
+// Work partition (row a.2), computed by every workgroup from the prefix lengths and, for a
+// ragged batch, the per-request tree lengths:
+//   * prefix lengths outside [0, max_prefix] and tree lengths outside [1, T] are errors; such a
+//     request and every later one are poisoned (their index segments can no longer be
+//     located) and get no keys; after a bad tree length they also get no rows, since the
+//     rows' positions depend on it;
+//   * node_off_b = exclusive scan of T_b (rows of request b start at node_off_b * H);
+//   * key_off_b = exclusive scan of (E_b + T_b), where E_b = ceil(P_b / page) is the number
 //     of prefix entries of the index segment (E_b = P_b when pages are single tokens);
 //   * split length S: fixed, or the smallest multiple of 32 (at least min_split) whose
 //     unit count stays within target_units (one workgroup per CU per M tile): first the
 //     even spread of the batch's prefix tokens and tree keys, then, if ragged requests
 //     round up past the target, a search upward from there;
 //   * units_b = max(1, ceil(P_b / S)) under a fixed split; under an automatic one the tree
-//     tiles count too, units_b = max(1, min(ceil((P_b + tree keys) / S), ceil(P_b / S) + 1));
+//     tiles count too, units_b = max(1, min(ceil((P_b + tree keys_b) / S), ceil(P_b / S) + 1));
 //     first_unit_b = exclusive scan of units_b.
-// Fills s_unit[] for unit g (request, key offset, P, first unit, units, error bits) and
-// returns the number of units.  The publishing workgroup also writes the plan out.
+// Fills s_unit[] for unit g (request, key offset, P, first unit, units, error bits, S, T_b,
+// node offset) and returns the number of units.  The publishing workgroup also writes the
+// plan out.
 struct UnitPlan {
   int b, key_off, prefix, first, units, split;
   uint32_t err;
@@ -289,30 +296,39 @@ __device__ int plan_units(const PartialArgs& a, int g, bool publish, int* s_tmp,
   const int tid = threadIdx.x;
   const int B = a.batch, T = a.T;
   constexpr int kPer = kMaxBatch / kThreads;  // requests per thread
-  int pv[kPer], bad[kPer];
+  int pv[kPer], tl[kPer], bad[kPer];
   int nbad = 0;
   // all of a thread's loads go out before the first wait (addresses clamped into the batch)
 #pragma unroll
   for (int j = 0; j < kPer; j++) pv[j] = a.prefix_lens[min(kPer * tid + j, B - 1)];
 #pragma unroll
+  for (int j = 0; j < kPer; j++) tl[j] = a.tree_lens ? a.tree_lens[min(kPer * tid + j, B - 1)] : T;
+  // bad prefix lengths count in the low 16 bits, bad tree lengths in the high ones (B <= 1024)
+#pragma unroll
   for (int j = 0; j < kPer; j++) {
     const int i = kPer * tid + j;
-    bad[j] = (i < B && (pv[j] < 0 || pv[j] > a.max_prefix)) ? 1 : 0;
-    if (i >= B) pv[j] = 0;
+    const int bp = (i < B && (pv[j] < 0 || pv[j] > a.max_prefix)) ? 1 : 0;
+    const int bt = (i < B && (tl[j] < 1 || tl[j] > T)) ? 1 : 0;
+    bad[j] = bp + (bt << 16);
+    if (i >= B) pv[j] = tl[j] = 0;
     nbad += bad[j];
   }
   int tot_bad;
   int run_bad = wg_exclusive_scan(nbad, s_tmp, tot_bad);
-  int segsum = 0, toksum = 0;
+  int segsum = 0, toksum = 0, nodesum = 0;
   uint32_t err[kPer];
 #pragma unroll
   for (int j = 0; j < kPer; j++) {
     run_bad += bad[j];
-    err[j] = run_bad > 0 ? kErrBadPrefix : 0u;
+    err[j] = ((run_bad & 0xFFFF) ? kErrBadPrefix : 0u) | ((run_bad >> 16) ? kErrBadTreeLen : 0u);
     if (err[j]) pv[j] = 0;
-    if (kPer * tid + j < B) segsum += seg_entries(pv[j], a.page_log2) + T;
+    if (err[j] & kErrBadTreeLen) tl[j] = 0;
+    if (kPer * tid + j < B) segsum += seg_entries(pv[j], a.page_log2) + tl[j];
     toksum += pv[j];
+    nodesum += tl[j];
   }
+  int total_nodes;
+  int node_off = wg_exclusive_scan(nodesum, s_tmp, total_nodes);
   int total_keys;
   int key_off = wg_exclusive_scan(segsum, s_tmp, total_keys);
   auto round_tile = [](int x) { return (x + kTileKeys - 1) / kTileKeys * kTileKeys; };
@@ -320,13 +336,14 @@ __device__ int plan_units(const PartialArgs& a, int g, bool publish, int* s_tmp,
   // Keys a request's units share: its prefix, plus its tree tiles under an automatic split,
   // so that the last unit (which also covers the tree) gets a smaller prefix share.  A
   // unit beyond the prefix units is allowed only as that last one.
-  const int tkeys = S > 0 ? 0 : round_tile(T);
-  auto units_of = [&](int p, int s) { return max(1, min((p + tkeys + s - 1) / s, (p + s - 1) / s + 1)); };
+  const bool fixed_split = a.split_fixed > 0;
+  auto tkeys_of = [&](int t) { return fixed_split ? 0 : round_tile(t); };
+  auto units_of = [&](int p, int tk, int s) { return max(1, min((p + tk + s - 1) / s, (p + s - 1) / s + 1)); };
   auto units_at = [&](int s, int* units) {  // this thread's units at split length s
     int us = 0;
 #pragma unroll
     for (int j = 0; j < kPer; j++) {
-      units[j] = (kPer * tid + j < B) ? units_of(pv[j], s) : 0;
+      units[j] = (kPer * tid + j < B) ? units_of(pv[j], tkeys_of(tl[j]), s) : 0;
       us += units[j];
     }
     return us;
@@ -336,10 +353,15 @@ __device__ int plan_units(const PartialArgs& a, int g, bool publish, int* s_tmp,
   if (S > 0) {
     first = wg_exclusive_scan(units_at(S, units), s_tmp, total_units);
   } else {
-    int total_prefix = total_keys - B * T;  // prefix tokens (entries are tokens without pages)
+    int total_prefix = total_keys - total_nodes;  // prefix tokens (entries are tokens without pages)
     if (a.page_log2 > 0) (void)wg_exclusive_scan(toksum, s_tmp, total_prefix);
+    int tksum = 0;  // the batch's tree keys, in whole tiles per request
+#pragma unroll
+    for (int j = 0; j < kPer; j++) tksum += tkeys_of(tl[j]);
+    int total_tkeys;
+    (void)wg_exclusive_scan(tksum, s_tmp, total_tkeys);
     const int U = a.target_units;
-    const int work = total_prefix + B * tkeys;
+    const int work = total_prefix + total_tkeys;
     S = max(a.min_split, round_tile((work + U - 1) / U));
     first = wg_exclusive_scan(units_at(S, units), s_tmp, total_units);
     if (total_units > U && B < U) {
@@ -355,7 +377,10 @@ __device__ int plan_units(const PartialArgs& a, int g, bool publish, int* s_tmp,
         // round tests up to kThreads lengths (spaced st apart) at once.
 #pragma unroll
         for (int j = 0; j < kPer; j++)
-          if (kPer * tid + j < B) s_scr[kPer * tid + j] = pv[j];
+          if (kPer * tid + j < B) {
+            s_scr[kPer * tid + j] = pv[j];
+            s_scr[kMaxBatch + kPer * tid + j] = tkeys_of(tl[j]);
+          }
         __syncthreads();
         while (lo < hi) {
           const int n = (hi - lo) / kTileKeys;  // lengths lo, lo + 32, ..., hi - 32 are open
@@ -365,7 +390,7 @@ __device__ int plan_units(const PartialArgs& a, int g, bool publish, int* s_tmp,
           bool fits = false;
           if (tid < m) {
             int us = 0;
-            for (int k = 0; k < B; k++) us += units_of(s_scr[k], c);
+            for (int k = 0; k < B; k++) us += units_of(s_scr[k], s_scr[kMaxBatch + k], c);
             fits = us <= U;
           }
           if (tid == 0) s_tmp[0] = kThreads;
@@ -404,6 +429,8 @@ __device__ int plan_units(const PartialArgs& a, int g, bool publish, int* s_tmp,
         s_unit[3] = first;
         s_unit[4] = units[j];
         s_unit[5] = (int)err[j];
+        s_unit[7] = tl[j];
+        s_unit[8] = node_off;
       }
       if (publish) {
         ReqPlan rp;
@@ -412,10 +439,13 @@ __device__ int plan_units(const PartialArgs& a, int g, bool publish, int* s_tmp,
         rp.first_unit = first;
         rp.units = units[j];
         rp.err = err[j];
-        rp.pad[0] = rp.pad[1] = rp.pad[2] = 0;
+        rp.tree_nodes = tl[j];
+        rp.node_off = node_off;
+        rp.pad = 0;
         a.req[i] = rp;
       }
-      key_off += seg_entries(pv[j], a.page_log2) + T;
+      key_off += seg_entries(pv[j], a.page_log2) + tl[j];
+      node_off += tl[j];
       first += units[j];
     }
   }
@@ -423,7 +453,7 @@ __device__ int plan_units(const PartialArgs& a, int g, bool publish, int* s_tmp,
     a.hdr->split_len = S;
     a.hdr->total_units = total_units;
     a.hdr->n_mtiles = a.n_mtiles;
-    if (tot_bad) atomicOr(a.sticky_err, kErrBadPrefix);
+    if (tot_bad) atomicOr(a.sticky_err, ((tot_bad & 0xFFFF) ? kErrBadPrefix : 0u) | ((tot_bad >> 16) ? kErrBadTreeLen : 0u));
   }
   s_unit[6] = S;  // same value in every thread
   __syncthreads();
@@ -490,15 +520,15 @@ template <bool kPaged>
     for (int tl = 0; tl < 2 && tl < ntiles; tl++) {
       const char* src = row_of(slot_of(tl, index_of(tl, kt), kt)) + kx * 16;
       const uint32_t d = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds + tl * kTileBytes) + wu * 1024);
-      lds_dma16<0>(src + 0 * 128, d);
-      lds_dma16<1>(src + 1 * 128, d);
-      lds_dma16<2>(src + 2 * 128, d);
-      lds_dma16<3>(src + 3 * 128, d);
-      lds_dma16<4>(src + 4 * 128, d);
-      lds_dma16<5>(src + 5 * 128, d);
-      lds_dma16<6>(src + 6 * 128, d);
-      lds_dma16<7>(src + 7 * 128, d);
-      lds_dma16<8>(src + 8 * 128, d);
+      lds_dma16<0>(src, d);
+      lds_dma16<1>(src, d);
+      lds_dma16<2>(src, d);
+      lds_dma16<3>(src, d);
+      lds_dma16<4>(src, d);
+      lds_dma16<5>(src, d);
+      lds_dma16<6>(src, d);
+      lds_dma16<7>(src, d);
+      lds_dma16<8>(src, d);
     }
   };
   auto tile0_barrier = [&]() {  // start_scores: tile 0 has landed everywhere
@@ -600,7 +630,7 @@ void k_partial(PartialArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[kTileBufs * kTileBytes + kWaves * kQLdsBytes];
   __shared__ int s_restart[2][kWaves];
   __shared__ int s_tmp[kWaves];
-  __shared__ int s_unit[8];
+  __shared__ int s_unit[10];
   lds_char* lds = (lds_char*)smem;
 
   const int tid = threadIdx.x;
@@ -623,6 +653,13 @@ void k_partial(PartialArgs a) {
     mt = bid % a.n_mtiles;
     g = bid / a.n_mtiles;
   }
+  // Workgroup 0's first wave samples the shader-cycle and wall-clock counters at its start and
+  // end, for the plan readback (the shader clock under load).
+  uint64_t clk0 = 0, rt0 = 0;
+  if (bid == 0 && wu == 0) {
+    clk0 = __builtin_amdgcn_s_memtime();
+    rt0 = __builtin_amdgcn_s_memrealtime();
+  }
   // (tile buffer 0 is the plan's scratch: no gather writes it before the plan is done)
   const int total_units = plan_units(a, g, g == 0 && mt == 0, s_tmp, s_unit, reinterpret_cast<int*>(smem));
   if (g >= total_units || g >= a.units_cap) return;
@@ -633,12 +670,15 @@ void k_partial(PartialArgs a) {
   const int nunits = s_unit[4];
   uint32_t req_err = (uint32_t)s_unit[5];
   const int S = s_unit[6];
+  const int Tb = s_unit[7];        // this request's tree nodes (the call's T unless ragged)
+  const int node_off = s_unit[8];  // its first row (node) in q / out / tree_parent
+  const int Mb = a.H * Tb;         // its query rows
   const int u = g - first_unit;
   const int kbeg = u * S;
   const int npk = max(0, min(S, prefix - kbeg));  // prefix keys of this unit
   const int npt = (npk + kTileKeys - 1) / kTileKeys;
   const bool last = (u == nunits - 1);
-  const int ntiles = npt + (last ? (a.T + kTileKeys - 1) / kTileKeys : 0);
+  const int ntiles = npt + (last ? (Tb + kTileKeys - 1) / kTileKeys : 0);
   // Prefix part of the index segment: per-token slots from this unit's first key on, or
   // the request's page ids (indexed by absolute prefix position); then the tree slots.
   const int32_t* __restrict__ pidx = a.kv_indices + key_off + (kPaged ? 0 : kbeg);
@@ -656,7 +696,7 @@ void k_partial(PartialArgs a) {
   constexpr int kW = kBigTree ? kMaxTreeWords : 1;
   uint64_t* s_m = reinterpret_cast<uint64_t*>(smem + 2 * kTileBytes);
   const int r = mt * kRowsPerBlock + w * kRowsPerWave + lrow;
-  const bool rvalid = r < a.M;
+  const bool rvalid = r < Mb;
 
   // Gather geometry: thread tid loads 9 chunks of key kt of every tile.
   const int kt = tid >> 3;
@@ -668,7 +708,7 @@ void k_partial(PartialArgs a) {
   // steps: load_index issues the table load, slot_of turns its value into the slot once it is
   // needed (a contiguous prefix run ignores the value), so no wait follows the load.
   auto key_of = [&](int t) -> int {
-    const int nv = t < npt ? min(kTileKeys, npk - t * kTileKeys) : min(kTileKeys, a.T - (t - npt) * kTileKeys);
+    const int nv = t < npt ? min(kTileKeys, npk - t * kTileKeys) : min(kTileKeys, Tb - (t - npt) * kTileKeys);
     return kt < nv ? kt : 0;
   };
   auto load_index = [&](int t) -> int {
@@ -693,15 +733,15 @@ void k_partial(PartialArgs a) {
   auto issue_piece = [&](const char* src, uint32_t dst, int j) {
     const uint32_t d = __builtin_amdgcn_readfirstlane(dst);
     switch (j) {  // j is a constant wherever this is inlined
-      case 0: lds_dma16<0>(src + 0 * 128, d); break;
-      case 1: lds_dma16<1>(src + 1 * 128, d); break;
-      case 2: lds_dma16<2>(src + 2 * 128, d); break;
-      case 3: lds_dma16<3>(src + 3 * 128, d); break;
-      case 4: lds_dma16<4>(src + 4 * 128, d); break;
-      case 5: lds_dma16<5>(src + 5 * 128, d); break;
-      case 6: lds_dma16<6>(src + 6 * 128, d); break;
-      case 7: lds_dma16<7>(src + 7 * 128, d); break;
-      default: lds_dma16<8>(src + 8 * 128, d); break;
+      case 0: lds_dma16<0>(src, d); break;
+      case 1: lds_dma16<1>(src, d); break;
+      case 2: lds_dma16<2>(src, d); break;
+      case 3: lds_dma16<3>(src, d); break;
+      case 4: lds_dma16<4>(src, d); break;
+      case 5: lds_dma16<5>(src, d); break;
+      case 6: lds_dma16<6>(src, d); break;
+      case 7: lds_dma16<7>(src, d); break;
+      default: lds_dma16<8>(src, d); break;
     }
   };
   auto issue_tile = [&](int bi, const char* src) {
@@ -716,6 +756,13 @@ void k_partial(PartialArgs a) {
     return kPaged ? page_slot(pidx[(kbeg + k) >> a.page_log2], kbeg + k) : pidx[k];
   };
 
+  // M tiles past this request's rows (a smaller tree than the call's largest) have no work.
+  // A request without rows (after a bad tree length) keeps only M tile 0's bookkeeping.
+  if (mt * kRowsPerBlock >= Mb && (mt > 0 || Mb == 0)) {
+    if (tid == 0 && mt == 0) a.unit_fast[g] = 0;
+    if (bid == 0 && tid == 0) a.hdr->clk_cycles = 0;
+    return;
+  }
   // Reads that depend only on the plan go out together: the run check's first keys, the
   // index entries of tiles 0..2 and the tree parents.  Q follows the first gathers (loads
   // complete in issue order, and the compiler's waits before the gathers cover every load
@@ -735,10 +782,10 @@ void k_partial(PartialArgs a) {
     if (ntiles > 2) raw2 = load_index(2);
   }
   int par_i = 0;
-  if (last && tid < a.T) par_i = a.tree_parent[(size_t)b * a.T + tid];
+  if (last && tid < Tb) par_i = a.tree_parent[(size_t)node_off + tid];
   int* s_jump = reinterpret_cast<int*>(smem + 2 * kTileBytes + kMaxTree * kMaxTreeWords * 8);
   auto masks = [&]() {
-    if (build_masks<kW>(par_i, a.T, s_m, s_jump)) {
+    if (build_masks<kW>(par_i, Tb, s_m, s_jump)) {
       req_err |= kErrBadParent;
       if (tid == 0 && mt == 0) atomicOr(a.sticky_err, kErrBadParent);
     }
@@ -750,6 +797,7 @@ void k_partial(PartialArgs a) {
     if (last) masks();  // its parents are still checked and reported
     poison();
     if (tid == 0 && mt == 0) a.unit_fast[g] = 0;
+    if (bid == 0 && tid == 0) a.hdr->clk_cycles = 0;
     return;
   }
 
@@ -822,26 +870,40 @@ void k_partial(PartialArgs a) {
   // PV MFMA, their sum, and the row's tile maximum (log2 units) for the reference check.
   struct Soft {
     float pe;  // probability of the even key of the pair being packed
-    float m;
     u32x4 pb[2];
     float psum;
-    float tmax;
   };
   // Step i (0..35) of that computation; the steps are spread between the score MFMAs of the
   // next tile so that the VALU work runs while the matrix core is busy.  Each probability
-  // is packed as soon as its pair is complete, so few of them are live at once.
+  // is packed as soon as its pair is complete, so few of them are live at once.  No maximum
+  // is taken here: a probability above 2^16 shows in the lane's sum, and only then (rarely)
+  // is the tile's maximum computed, for the reference test (see `restart_test`).
   auto soft_step = [&](Soft& o, const f32x16& sc, float nm, int i) {
     if (i < 16) {
       const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], c2, nm));
-      o.m = i == 0 ? sc[0] : fmaxf(o.m, sc[i]);
       o.psum = i == 0 ? e : o.psum + e;
       if (i & 1)
         o.pb[i >> 3][(i >> 1) & 3] = pack_bf16x2(o.pe, e);
       else
         o.pe = e;
-    } else if (i == 16) {
-      o.tmax = xhalf_max(o.m) * c2;
     }
+  };
+  // After the softmax of tile t (scores sc): if some row's tile maximum exceeds its reference
+  // by more than 16 (log2 units), raise the reference to it and flag the wave, so that every
+  // wave restarts the unit at the next barrier.  A lane's sum of 16 probabilities exceeds
+  // 2^16 whenever one of them does, so the maximum is only needed when a sum does.
+  auto restart_test = [&](const f32x16& sc, float psum) -> bool {
+    bool trig = false;
+    if (__builtin_expect(__any(psum > 65536.0f), 0)) {
+      float m = sc[0];
+#pragma unroll
+      for (int v = 1; v < 16; v++) m = fmaxf(m, sc[v]);
+      const float tmax = xhalf_max(m) * c2;
+      const bool raise = mref != -INFINITY && tmax > mref + 16.0f;
+      trig = __any(raise);
+      if (raise) mref = tmax;  // the pass is abandoned at the next barrier; keep the larger reference
+    }
+    return trig;
   };
 
   // One chain of 36 score MFMAs over the tile at kb.  Optionally interleaves the softmax
@@ -909,10 +971,21 @@ void k_partial(PartialArgs a) {
       vr[mf] = __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     }
   };
-  auto pv_tile = [&](const lds_char* kb, const u32x4 (&pb)[2], const u32x4 (&vc0)[2]) {
+  // PV of a tile is split: the head runs d-blocks 0 .. 15 - kDefer and reads the V fragments
+  // of the last kDefer blocks (vd); their MFMAs (pv_deferred) run after the next barrier,
+  // while the first score operands of the next tile come in from LDS, so that the matrix core
+  // has work across the barrier.  The fragments are read before that barrier, which is what
+  // keeps them clear of the gathers that later overwrite the tile's buffer.
+  // (none for big trees, whose four-word masks leave too few registers)
+  constexpr int kDefer = kBigTree ? 0 : 2;
+  constexpr int kDeferArr = kDefer > 0 ? kDefer : 1;
+  auto pv_head = [&](const lds_char* kb, const u32x4 (&pb)[2], const u32x4 (&vc0)[2], u32x4 (&vd)[kDeferArr][2]) {
+    // the asm MFMAs insert no wait states: two between the last VALU write of P and its use
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 1");
     u32x4 vc[2] = {vc0[0], vc0[1]};
 #pragma unroll
-    for (int db = 0; db < 16; db++) {
+    for (int db = 0; db < 16 - kDefer; db++) {
       u32x4 vn[2];
       if (db + 1 < 16) load_v(kb, db + 1, vn);
       pv_mfma(db, vc[0], pb[0]);
@@ -922,11 +995,25 @@ void k_partial(PartialArgs a) {
         vc[1] = vn[1];
       }
     }
+    if constexpr (kDefer > 0) {
+      vd[0][0] = vc[0];
+      vd[0][1] = vc[1];
+#pragma unroll
+      for (int k = 1; k < kDefer; k++) load_v(kb, 16 - kDefer + k, vd[k]);
+    }
+  };
+  auto pv_deferred = [&](const u32x4 (&vd)[kDeferArr][2], const u32x4 (&pb)[2]) {
+#pragma unroll
+    for (int k = 0; k < kDefer; k++) {
+      pv_mfma(16 - kDefer + k, vd[k][0], pb[0]);
+      pv_mfma(16 - kDefer + k, vd[k][1], pb[1]);
+    }
   };
 
   // Software pipeline over the tiles of the unit, three LDS buffers in rotation (tile t in
-  // buffer bi).  Iteration t: S(t+1) runs on the matrix core while the softmax of tile t
-  // runs in the gaps, and the gathers of tile t+2 are issued; then PV(t).
+  // buffer bi).  Iteration t, after the barrier that makes tile t+1 visible: the deferred PV
+  // blocks of tile t-1, then S(t+1) on the matrix core with the softmax of tile t in its gaps
+  // and the gathers of tile t+2 among its MFMAs, then the head of PV(t).
   int t = 0, bi = 0;
   bool need_init = true;  // some row of the wave has no reference yet
   int idx_next = 0;  // this thread's loaded index-table entry of tile t+2
@@ -969,7 +1056,8 @@ void k_partial(PartialArgs a) {
   {
     u32x4 qt[36 - kQReg];
     // rows past M (last M tile) read the request's last row; their results are dropped
-    const u32x4* qp = reinterpret_cast<const u32x4*>(a.q + ((size_t)b * a.M + (rvalid ? r : a.M - 1)) * kLatent) + h;
+    const u32x4* qp =
+        reinterpret_cast<const u32x4*>(a.q + ((size_t)node_off * a.H + (rvalid ? r : Mb - 1)) * kLatent) + h;
 #pragma unroll
     for (int kk = 0; kk < kQReg; kk++) qf[kk] = qp[2 * kk];
 #pragma unroll
@@ -991,81 +1079,92 @@ void k_partial(PartialArgs a) {
       // audit lets the compiler use AGPRs past this marker.
       asm volatile("; mlv-helper-waves" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);  // keep the helper's code below the marker
-      gather_helper<kPaged>(reinterpret_cast<const char*>(a.pool), a.row_stride_bytes, a.pool_slots, a.T,
+      gather_helper<kPaged>(reinterpret_cast<const char*>(a.pool), a.row_stride_bytes, a.pool_slots, Tb,
                             a.page_log2, a.max_page, pidx, tidx, kbeg, npk, npt, ntiles, run_base, bad_index, smem,
                             &s_restart[0][0]);
       return;
     }
   }
   start_scores();
-  for (;;) {
+  // Deferred PV fragments and their P operand; zero before a pass's first tile, so that the
+  // deferred MFMAs at its first barrier add nothing.
+  u32x4 vdef[kDeferArr][2], pdef[2];
+  auto clear_deferred = [&]() {
+#pragma unroll
+    for (int k = 0; k < kDeferArr; k++) vdef[k][0] = vdef[k][1] = u32x4{0u, 0u, 0u, 0u};
+    pdef[0] = pdef[1] = u32x4{0u, 0u, 0u, 0u};
+  };
+  clear_deferred();
+  // Tiles t with t + 3 < nfull (all of t .. t+3 are full prefix tiles) take the steady body:
+  // no tail or tree masks, no clamped keys, no first-reference step.
+  const int nfull = npk / kTileKeys;
+  // One iteration; returns 0 to go on, 1 at the end of the unit, 2 for a restart.
+  auto iteration = [&](auto steady) -> int {
+    constexpr bool kSteady = decltype(steady)::value != 0;
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's loads of tile t+1 landed
     __syncthreads();                     // ... and everyone's; PV(t-1) finished everywhere
     // Reads that need only the barrier go out first (the restart flags of tile t-1 and the
-    // first fragments of S(t+1)); the index and address work below covers their latency.
-    // The rare cases (restart, end, masked tiles, first reference) are marked cold so that
-    // the steady state runs straight through.
+    // first fragments of S(t+1)); the deferred PV MFMAs of tile t-1 cover their latency.
     const int b1 = bi == kTileBufs - 1 ? 0 : bi + 1;
     const int b2 = b1 == kTileBufs - 1 ? 0 : b1 + 1;
     const lds_char* kb1 = lds + b1 * kTileBytes;
     const int* fl = s_restart[(t - 1) & 1];
     const int flags = fl[0] | fl[1] | fl[2] | fl[3];
     const SPre pre = s_pre(kb1);
+    pv_deferred(vdef, pdef);
     // Gathers of tile t+2 go to buffer b2 (on the last tiles they re-read pool row 0 into it;
     // nothing reads that buffer before the next barrier).
     const char* pf_src = nullptr;
     uint32_t pf_dst = 0;
     if (!kHelp) {
-      pf_src = tile_src(t + 2 < ntiles ? slot_of(t + 2, idx_next) : 0);
+      if (kSteady && !kPaged) {  // full tiles: no clamped keys
+        pf_src = tile_src(run_base >= 0 ? run_base + (t + 2) * kTileKeys + kt : idx_next);
+        idx_next = pidx[(t + 3) * kTileKeys + kt];
+      } else {
+        pf_src = tile_src(t + 2 < ntiles ? slot_of(t + 2, idx_next) : 0);
+        if (t + 3 < ntiles) idx_next = load_index(t + 3);
+      }
       pf_dst = tile_dst(b2);
-      if (t + 3 < ntiles) idx_next = load_index(t + 3);
     }
     const bool prev_flags = t > 0 && flags != 0;  // some wave raised its reference at tile t-1
-    if (__builtin_expect(t == ntiles || prev_flags, 0)) {
-      if (!prev_flags) break;
-      // the pass starts over with the raised references
-      asm volatile("s_nop 15\n\ts_nop 3" ::: "memory");  // PV MFMAs of the last tile have landed
-      MLV_ZERO_O();
-      lrun = 0.f;
-      {
-        const int e0 = load_index(0), e1 = ntiles > 1 ? load_index(1) : 0, e2 = ntiles > 2 ? load_index(2) : 0;
-        start_gathers(e0, e1, e2);
-        start_scores();
+    if (kSteady) {
+      if (__builtin_expect(prev_flags, 0)) return 2;
+    } else {
+      if (__builtin_expect(t == ntiles || prev_flags, 0)) return prev_flags ? 2 : 1;
+      // Tail and tree tiles: invisible keys get -inf (key of register v is 4h + 8(v/4) + v%4).
+      const bool tree = t >= npt;
+      const int tt = t - npt;
+      const int nv = tree ? min(kTileKeys, Tb - tt * kTileKeys) : min(kTileKeys, npk - t * kTileKeys);
+      if (__builtin_expect(tree || nv < kTileKeys, 0)) {
+        // the word holding tree tile tt's 32 keys (masked ORs: a select chain over the array
+        // is turned into an indexed private copy of it)
+        uint64_t aw = 0;
+#pragma unroll
+        for (int w = 0; w < kW; w++) aw |= anc[w] & (0ull - (uint64_t)((tt >> 1) == w));
+        const uint32_t win = tree ? (uint32_t)(aw >> ((tt & 1) * kTileKeys)) : ~0u;
+        const uint32_t tm = win >> (4 * h);
+        const int nvh = nv - 4 * h;
+#pragma unroll
+        for (int v = 0; v < 16; v++) {
+          const int kv = 8 * (v >> 2) + (v & 3);
+          sacc[v] = (kv < nvh && ((tm >> kv) & 1u)) ? sacc[v] : -INFINITY;
+        }
       }
-      continue;
-    }
-
-    // Tail and tree tiles: invisible keys get -inf (key of register v is 4h + 8(v/4) + v%4).
-    const bool tree = t >= npt;
-    const int tt = t - npt;
-    const int nv = tree ? min(kTileKeys, a.T - tt * kTileKeys) : min(kTileKeys, npk - t * kTileKeys);
-    if (__builtin_expect(tree || nv < kTileKeys, 0)) {
-      uint64_t aw = anc[0];  // the word holding tree tile tt's 32 keys
+      // A row's first visible keys set its reference (it may stay -inf if the tile hides all).
+      if (__builtin_expect(need_init, 0)) {
+        float m0 = sacc[0];
 #pragma unroll
-      for (int w = 1; w < kW; w++) aw = (tt >> 1) == w ? anc[w] : aw;
-      const uint32_t win = tree ? (uint32_t)(aw >> ((tt & 1) * kTileKeys)) : ~0u;
-      const uint32_t tm = win >> (4 * h);
-      const int nvh = nv - 4 * h;
-#pragma unroll
-      for (int v = 0; v < 16; v++) {
-        const int kv = 8 * (v >> 2) + (v & 3);
-        sacc[v] = (kv < nvh && ((tm >> kv) & 1u)) ? sacc[v] : -INFINITY;
+        for (int v = 1; v < 16; v++) m0 = fmaxf(m0, sacc[v]);
+        m0 = xhalf_max(m0) * c2;
+        if (mref == -INFINITY) mref = m0;
+        need_init = __any(mref == -INFINITY);
       }
     }
-    // A row's first visible keys set its reference (it may stay -inf if the tile hides all).
-    if (__builtin_expect(need_init, 0)) {
-      float m0 = sacc[0];
-#pragma unroll
-      for (int v = 1; v < 16; v++) m0 = fmaxf(m0, sacc[v]);
-      m0 = xhalf_max(m0) * c2;
-      if (mref == -INFINITY) mref = m0;
-      need_init = __any(mref == -INFINITY);
-    }
-    const float nm = mref == -INFINITY ? 0.f : -mref;  // all scores are -inf while mref is
+    const float nm = kSteady ? -mref : (mref == -INFINITY ? 0.f : -mref);  // all scores are -inf while mref is
 
     Soft so;
     f32x16 snext;
-    if (__builtin_expect(t + 1 < ntiles, 1)) {
+    if (kSteady || __builtin_expect(t + 1 < ntiles, 1)) {
       if constexpr (kHelp)  // the helper waves gather
         snext = s_chain(IntC<-1>{}, IntC<1>{}, kb1, nullptr, 0u, sacc, nm, so, pre);
       else
@@ -1078,18 +1177,43 @@ void k_partial(PartialArgs a) {
     const lds_char* kb = lds + bi * kTileBytes;
     u32x4 vc0[2];
     load_v(kb, 0, vc0);
-    const bool raise = mref != -INFINITY && so.tmax > mref + 16.0f;
-    const bool trig = __any(raise);
-    s_restart[t & 1][w] = trig ? 1 : 0;
-    if (raise) mref = so.tmax;  // the pass is abandoned at the next barrier; keep the larger reference
+    s_restart[t & 1][w] = restart_test(sacc, so.psum) ? 1 : 0;
     lrun += so.psum;
-    pv_tile(kb, so.pb, vc0);
+    pv_head(kb, so.pb, vc0, vdef);
+    pdef[0] = so.pb[0];
+    pdef[1] = so.pb[1];
     sacc = snext;
     bi = b1;
     t++;
+    return 0;
+  };
+  for (;;) {
+    int c;
+    do {
+      if (t + 3 < nfull && !need_init)
+        c = iteration(IntC<1>{});
+      else
+        c = iteration(IntC<0>{});
+    } while (c == 0);
+    if (c == 1) break;
+    // the pass starts over with the raised references
+    asm volatile("s_nop 15\n\ts_nop 3" ::: "memory");  // PV MFMAs of the last tile have landed
+    MLV_ZERO_O();
+    lrun = 0.f;
+    clear_deferred();
+    const int e0 = load_index(0), e1 = ntiles > 1 ? load_index(1) : 0, e2 = ntiles > 2 ? load_index(2) : 0;
+    start_gathers(e0, e1, e2);
+    start_scores();
   }
 
   asm volatile("s_nop 15\n\ts_nop 3" ::: "memory");  // last PV MFMA results settle before reads
+  if (bid == 0 && wu == 0) {
+    const uint64_t clk1 = __builtin_amdgcn_s_memtime(), rt1 = __builtin_amdgcn_s_memrealtime();
+    if (lane == 0) {
+      a.hdr->clk_cycles = (uint32_t)(clk1 - clk0);
+      a.hdr->clk_ticks = (uint32_t)(rt1 - rt0);
+    }
+  }
   const int any_bad = __syncthreads_or(bad_index);
   if (any_bad && tid == 0) atomicOr(a.sticky_err, kErrBadIndex);
   const float lt = xhalf_sum(lrun);
@@ -1175,6 +1299,8 @@ __global__ __launch_bounds__(256) void k_merge(MergeArgs a) {
   const int cl = lane % kLanes, slot = w * kGroups + lane / kLanes;
   const int b = row / a.M, r = row - b * a.M;
   ReqPlan R = a.req[b];
+  if (r >= R.tree_nodes * a.H) return;  // past this request's rows (ragged trees)
+  const size_t orow = (size_t)R.node_off * a.H + r;  // the row in out / lse
   R.first_unit = min(max(R.first_unit, 0), a.units_cap);  // never index past the partial buffers
   R.units = min(R.units, a.units_cap - R.first_unit);
   const float* pl = a.part_lse + (size_t)R.first_unit * a.M + r;
@@ -1239,10 +1365,10 @@ __global__ __launch_bounds__(256) void k_merge(MergeArgs a) {
       o[0] += s_acc[q][c];
       o[1] += s_acc[q][c + 1];
     }
-    reinterpret_cast<uint32_t*>(a.out + (size_t)row * kVdim + c0 + c)[0] =
+    reinterpret_cast<uint32_t*>(a.out + orow * kVdim + c0 + c)[0] =
         bf16_rne_bits(o[0] * inv) | (bf16_rne_bits(o[1] * inv) << 16);
   }
-  if (c0 == 0 && tid == 0) a.lse[row] = (m + __builtin_amdgcn_logf(Z)) * 0.69314718055994531f;
+  if (c0 == 0 && tid == 0) a.lse[orow] = (m + __builtin_amdgcn_logf(Z)) * 0.69314718055994531f;
 }
 
 // ------------------------------------------------------------------------------------------

@@ -36,6 +36,7 @@ constexpr uint32_t kErrBadParent = 0x1u;
 constexpr uint32_t kErrBadIndex = 0x2u;
 constexpr uint32_t kErrBadPrefix = 0x4u;
 constexpr uint32_t kErrConflict = 0x8u;   // a relocation destination is out of the pool or in use
+constexpr uint32_t kErrBadTreeLen = 0x10u; // a per-request tree length outside [1, T]
 
 struct PlanHeader {
   int32_t split_len;     // prefix tokens per split unit
@@ -43,7 +44,9 @@ struct PlanHeader {
   int32_t n_mtiles;      // 128-row tiles per request
   int32_t pad0;
   uint32_t sticky_err;   // OR of every data error since the last readback
-  uint32_t pad1[59];     // header is 256 bytes
+  uint32_t clk_cycles;   // shader-clock cycles of workgroup 0's first wave over its run (0: not sampled)
+  uint32_t clk_ticks;    // constant-rate wall-clock ticks over the same interval
+  uint32_t pad1[57];     // header is 256 bytes
 };
 static_assert(sizeof(PlanHeader) == 256, "header size");
 
@@ -52,8 +55,10 @@ struct ReqPlan {
   int32_t prefix_len;   // P_b after validation (0 when invalid)
   int32_t first_unit;   // global index of its first split unit
   int32_t units;        // number of split units (the last one also covers the tree)
-  uint32_t err;         // prefix-length error bits of this request
-  int32_t pad[3];
+  uint32_t err;         // prefix-length / tree-length error bits of this request
+  int32_t tree_nodes;   // T_b (0 when a tree length at or before this request is invalid)
+  int32_t node_off;     // first row (node) of the request in q / out / lse / tree_parent
+  int32_t pad;
 };
 static_assert(sizeof(ReqPlan) == 32, "ReqPlan size");
 
@@ -63,6 +68,7 @@ struct PartialArgs {
   const int32_t* kv_indices;
   const int32_t* prefix_lens;
   const int32_t* tree_parent;
+  const int32_t* tree_lens;  // [batch] per-request tree sizes T_b <= T, or null: every request has T
   PlanHeader* hdr;       // plan published by workgroup 0 (for the merge and readback)
   ReqPlan* req;
   uint16_t* part_o;      // [units, M, 512] unit-normalised partial outputs (bf16 bits)
@@ -71,7 +77,7 @@ struct PartialArgs {
   uint32_t* sticky_err;
   int64_t pool_slots;
   int64_t row_stride_bytes;
-  int32_t batch, T, H, M, n_mtiles;
+  int32_t batch, T, H, M, n_mtiles;  // T: the call's largest tree, M = H * T rows per unit
   int32_t max_prefix, split_fixed, target_units, min_split, units_cap;
   float scale_log2;      // sm_scale * log2(e), > 0
   uint32_t flags;
@@ -86,7 +92,7 @@ struct MergeArgs {
   const float* part_lse;
   uint16_t* out;
   float* lse;
-  int32_t batch, M, units_cap;
+  int32_t batch, H, M, units_cap;  // M = H * (the call's largest T): the partials' row stride
 };
 
 // Tier-1 relocation of prefix rows (relocate.hip).
@@ -127,6 +133,8 @@ hipError_t launch_accept(const AcceptArgs& a, hipStream_t s);
 int accept_chunks(int64_t vocab);
 hipError_t launch_partial(const PartialArgs& a, int grid, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
+hipError_t launch_probe_gather(const void* pool, int64_t stride_bytes, int64_t slots, const int32_t* idx, int n,
+                               int lds, int grid, uint32_t* sink, hipStream_t s);
 hipError_t launch_tree_masks(const int32_t* tree_parent, int batch, int T, uint64_t* masks, uint32_t* err,
                              hipStream_t s);
 

@@ -12,8 +12,10 @@ from .mla_tree_oracle import (  # noqa: F401
     bf16_to_f64,
     brute_force_verify_attention,
     lse_merge,
+    node_offsets,
     request_offsets,
     validate_parents,
     verify_attention,
+    verify_attention_ragged,
     visible_slots,
 )

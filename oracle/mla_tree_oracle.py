@@ -229,6 +229,52 @@ def verify_attention(q, pool, kv_indices, prefix_lens, tree_parent, sm_scale: fl
     return out, lse
 
 
+def node_offsets(tree_lens) -> np.ndarray:
+    """First packed row (node) of each request when requests have T_b = tree_lens[b] nodes:
+    the exclusive prefix sum of tree_lens."""
+    tl = np.asarray(tree_lens, dtype=np.int64)
+    return np.concatenate([[0], np.cumsum(tl)[:-1]]).astype(np.int64)
+
+
+def verify_attention_ragged(q, pool, kv_indices, prefix_lens, tree_lens, tree_parent, sm_scale: float):
+    """Tree-verify attention for a batch whose requests draft trees of different sizes.
+
+    Request b has T_b = tree_lens[b] >= 1 nodes.  Rows are packed request after request:
+    node i of request b is row n_b + i (n_b = node_offsets(tree_lens)[b]) of q [sum T_b, H, 576]
+    and of the results; tree_parent [sum T_b] holds, at n_b + i, the parent of node i within
+    its request (-1 for a root, else an earlier node of the same request).  Request b owns
+    kv_indices[off_b : off_b + P_b + T_b], its prefix slots then the slots of its tree nodes,
+    with off_b the exclusive prefix sum of P_b + T_b.  Each request is the definition above
+    with T = T_b (no node of one request sees another request's nodes), so the result is the
+    per-request attention written into the packed rows.
+    Returns out float64 [sum T_b, H, 512] and lse float64 [sum T_b, H].
+    """
+    q = np.asarray(q)
+    tree_lens = np.asarray(tree_lens, dtype=np.int64)
+    prefix_lens = np.asarray(prefix_lens, dtype=np.int64)
+    kv_indices = np.asarray(kv_indices)
+    tree_parent = np.asarray(tree_parent)
+    if np.any(tree_lens < 1):
+        raise ValueError("every request needs at least one tree node")
+    total = int(tree_lens.sum())
+    if q.shape[0] != total or len(tree_parent) != total:
+        raise ValueError("q and tree_parent must hold sum(tree_lens) rows")
+    if len(kv_indices) != int(prefix_lens.sum() + tree_lens.sum()):
+        raise ValueError("kv_indices length must be sum(P_b + T_b)")
+    h = q.shape[1]
+    out = np.zeros((total, h, VDIM))
+    lse = np.zeros((total, h))
+    nodes = node_offsets(tree_lens)
+    off = 0
+    for b in range(len(tree_lens)):
+        p, t, n = int(prefix_lens[b]), int(tree_lens[b]), int(nodes[b])
+        o, l = verify_attention(q[n:n + t], pool, kv_indices[off:off + p + t], np.array([p]),
+                                tree_parent[None, n:n + t], sm_scale)
+        out[n:n + t], lse[n:n + t] = o, l
+        off += p + t
+    return out, lse
+
+
 def attention_weights(q, pool, kv_indices, prefix_lens, tree_parent, sm_scale: float, b: int, i: int):
     """Softmax weights of node i of request b over Vis(b, i), float64 [H, |Vis|] (for the row-sum pin)."""
     t = np.asarray(tree_parent).shape[1]

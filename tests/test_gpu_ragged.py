@@ -1,0 +1,99 @@
+"""GPU parity of the ragged verify pass (mlaverify_run_ragged: a tree size per request, rows
+packed request after request) against the CPU fp64 oracle's ragged definition, through the
+C ABI.  Every request is drawn on its own from the workload recipe and the batch is packed
+(rows, parents, index segments), with all requests reading one shared pool."""
+
+import numpy as np
+import pytest
+import torch
+
+import mla_tree_verify_mlaverify_amd as mv
+from gpu_util import DEV, bf16, compare, i32
+from oracle import mla_tree_oracle as orc
+from workloads import synth
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+def ragged_case(seed, prefix, tree_lens, heads, slots, q_scale=1.0):
+    parts = [synth.small_config(seed + 7 * b, batch=1, prefix=[p], tree_nodes=t, heads=heads, slots=slots,
+                                tree="forest" if b % 3 == 2 else "random", q_scale=q_scale)
+             for b, (p, t) in enumerate(zip(prefix, tree_lens))]
+    return dict(q=np.concatenate([c["q"] for c in parts]), pool=parts[0]["pool"],
+                kv_indices=np.concatenate([c["kv_indices"] for c in parts]).astype(np.int32),
+                prefix_lens=np.array(prefix, dtype=np.int32), tree_lens=np.array(tree_lens, dtype=np.int32),
+                tree_parent=np.concatenate([c["tree_parent"][0] for c in parts]).astype(np.int32),
+                heads=heads, slots=slots, sm_scale=parts[0]["sm_scale"])
+
+
+def run_ragged(case, max_t=None, split=0, v=None, out_fill=None):
+    max_t = max_t or int(case["tree_lens"].max())
+    v = v or mv.Verifier(num_heads=case["heads"], max_batch=len(case["prefix_lens"]), max_tree_nodes=max_t,
+                         max_prefix_len=max(1, int(case["prefix_lens"].max())), pool_slots=case["slots"],
+                         sm_scale=case["sm_scale"], split_tokens=split, device=DEV)
+    rows = case["q"].shape[0]
+    out = torch.full((rows, case["heads"], 512), out_fill if out_fill is not None else float("nan"),
+                     dtype=torch.bfloat16, device=DEV)
+    lse = torch.full((rows, case["heads"]), out_fill if out_fill is not None else float("nan"), dtype=torch.float32,
+                     device=DEV)
+    v.run_ragged(bf16(case["q"]), bf16(case["pool"]), i32(case["kv_indices"]), i32(case["prefix_lens"]),
+                 i32(case["tree_lens"]), i32(case["tree_parent"]), max_t, out=out, lse=lse)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy(), lse.cpu().numpy(), v
+
+
+def oracle(case):
+    return orc.verify_attention_ragged(case["q"], case["pool"], case["kv_indices"], case["prefix_lens"],
+                                       case["tree_lens"], case["tree_parent"], case["sm_scale"])
+
+
+@pytest.mark.parametrize("seed,prefix,tree_lens,heads,split", [
+    (80, [3000, 1, 700, 4096], [1, 5, 64, 200], 8, 0),     # big-tree launch (max 200): four mask words
+    (81, [1500, 0, 257, 33, 9000], [64, 5, 1, 17, 33], 8, 0),
+    (82, [1500, 0, 257, 33, 9000], [64, 5, 1, 17, 33], 8, 256),
+    (83, [4000, 100, 2000], [8, 1, 3], 8, 0),                # one M tile: the helper-wave gathers
+    (84, [640] * 6, [2, 31, 32, 33, 63, 64], 16, 0),         # tile and M-tile edges
+])
+def test_ragged_parity(seed, prefix, tree_lens, heads, split):
+    case = ragged_case(seed, prefix, tree_lens, heads, slots=max(4096, 2 * (sum(prefix) + sum(tree_lens))))
+    out, lse, v = run_ragged(case, split=split)
+    assert v.read_device_errors() == 0
+    ref_out, ref_lse = oracle(case)
+    print(compare(out, lse, ref_out, ref_lse))
+
+
+def test_ragged_with_equal_trees_is_run_bit_for_bit():
+    cfg = synth.small_config(85, batch=3, prefix=[1000, 20, 333], tree_nodes=24, heads=8, slots=8192, q_scale=1.0)
+    case = dict(q=cfg["q"], pool=cfg["pool"], kv_indices=cfg["kv_indices"], prefix_lens=cfg["prefix_lens"],
+                tree_lens=np.full(3, 24, dtype=np.int32), tree_parent=cfg["tree_parent"].reshape(-1),
+                heads=8, slots=8192, sm_scale=cfg["sm_scale"])
+    out, lse, v = run_ragged(case)
+    o2, l2 = v.run(bf16(cfg["q"]), bf16(cfg["pool"]), i32(cfg["kv_indices"]), i32(cfg["prefix_lens"]),
+                   i32(cfg["tree_parent"]))
+    torch.cuda.synchronize()
+    assert np.array_equal(out, o2.float().cpu().numpy()) and np.array_equal(lse, l2.cpu().numpy())
+
+
+def test_ragged_below_the_launch_maximum():
+    # max_T of the call (96, a big-tree launch) above every request's tree
+    case = ragged_case(86, [500, 1200], [7, 40], 4, slots=4096)
+    out, lse, _ = run_ragged(case, max_t=96)
+    ref_out, ref_lse = oracle(case)
+    compare(out, lse, ref_out, ref_lse)
+
+
+def test_bad_tree_length_poisons_that_request_and_later_ones():
+    case = ragged_case(87, [300, 400, 500], [4, 6, 5], 8, slots=4096)
+    bad = dict(case, tree_lens=np.array([4, 9, 5], dtype=np.int32))  # 9 > max_T = 6
+    out, lse, v = run_ragged(bad, max_t=6, out_fill=7.0)
+    assert v.read_device_errors() == mv.DEVERR_BAD_TREE_LEN
+    ref_out, ref_lse = orc.verify_attention_ragged(case["q"][:4], case["pool"], case["kv_indices"][:304],
+                                                   case["prefix_lens"][:1], [4], case["tree_parent"][:4],
+                                                   case["sm_scale"])
+    compare(out[:4], lse[:4], ref_out, ref_lse)  # the request before the bad one is whole
+    assert np.all(out[4:] == 7.0) and np.all(lse[4:] == 7.0)  # no row of the later ones is written
+    zero = dict(case, tree_lens=np.array([4, 0, 5], dtype=np.int32))
+    out, lse, v = run_ragged(zero, max_t=6, out_fill=7.0)
+    assert v.read_device_errors() == mv.DEVERR_BAD_TREE_LEN
+    compare(out[:4], lse[:4], ref_out, ref_lse)
+    assert np.all(out[4:] == 7.0) and np.all(lse[4:] == 7.0)

@@ -175,6 +175,26 @@ def test_f32_to_bf16_round_to_nearest_even():
     assert (b[7] & 0x7F80) == 0x7F80 and (b[7] & 0x007F) != 0
 
 
+def test_f32_to_bf16_extremes_and_nearest():
+    x = np.array([3.4028235e38, -3.4028235e38, -np.inf, 1e-45, -1e-45, 0.0, -0.0], dtype=np.float32)
+    b = synth.f32_to_bf16_bits(x)
+    assert b.tolist() == [0x7F80, 0xFF80, 0xFF80, 0x0000, 0x8000, 0x0000, 0x8000]
+    n = synth.f32_to_bf16_bits(np.array([-np.nan], dtype=np.float32))[0]
+    assert (n & 0x8000) and (n & 0x7F80) == 0x7F80 and (n & 0x7F)
+    # every finite result is a nearest bf16 value (checked against both neighbours), ties to even
+    rng = np.random.default_rng(3)
+    x = (rng.standard_normal(200000) * np.exp(rng.uniform(-80, 80, 200000))).astype(np.float32)
+    x = x[np.isfinite(x) & (np.abs(x) < 3.0e38)]
+    b = synth.f32_to_bf16_bits(x).astype(np.int64)
+    got = orc.bf16_to_f64(b.astype(np.uint16))
+    xd = x.astype(np.float64)
+    for nb in (b - 1, b + 1):
+        ok = (nb & 0x7F80) != 0x7F80  # neighbours that are finite bf16 patterns
+        other = orc.bf16_to_f64((nb & 0xFFFF).astype(np.uint16))
+        d, dn = np.abs(xd - got), np.abs(xd - other)
+        assert np.all(~ok | (np.sign(other) != np.sign(got)) | (d < dn) | ((d == dn) & (b % 2 == 0)))
+
+
 def test_generator_is_deterministic_and_shaped():
     a = synth.make_config(0)
     b = synth.make_config(0)
@@ -355,6 +375,25 @@ def test_softmax_rows_sum_to_one():
         assert np.all(w >= 0)
 
 
+def test_attention_weights_reproduce_the_output():
+    """The weights of Vis(b, i), applied to the visible V rows, give verify_attention's row (pinned
+    against SDPA and brute force above), and the log of the weights of two keys differs by their
+    score difference; with sharp queries a wrong scale or a dropped key fails both."""
+    cfg = synth.small_config(13, batch=2, prefix=[50, 3], tree_nodes=6, heads=3, slots=512, q_scale=3.0)
+    out, lse = orc.verify_attention(cfg["q"], cfg["pool"], cfg["kv_indices"], cfg["prefix_lens"],
+                                    cfg["tree_parent"], SCALE)
+    for b in range(2):
+        for i in range(6):
+            w = orc.attention_weights(cfg["q"], cfg["pool"], cfg["kv_indices"], cfg["prefix_lens"],
+                                      cfg["tree_parent"], SCALE, b, i)
+            slots = orc.visible_slots(cfg["kv_indices"], cfg["prefix_lens"], cfg["tree_parent"], b, i)
+            kv = orc.bf16_to_f64(cfg["pool"][slots, :576])
+            np.testing.assert_allclose(w @ kv[:, :512], out[b * 6 + i], rtol=1e-12, atol=1e-14)
+            s = SCALE * orc.bf16_to_f64(cfg["q"][b * 6 + i]) @ kv.T
+            np.testing.assert_allclose(np.log(w[:, 1:]) - np.log(w[:, :1]), s[:, 1:] - s[:, :1], rtol=0, atol=1e-10)
+            np.testing.assert_allclose(np.log(w), s - lse[b * 6 + i][:, None], rtol=0, atol=1e-10)
+
+
 def test_prefix_order_invariance():
     cfg = synth.small_config(11, batch=2, prefix=[64, 31], tree_nodes=8, heads=2, slots=512)
     shuf = synth.permute_prefix(cfg, np.random.default_rng(5))
@@ -428,3 +467,69 @@ def test_paged_layout_attention_equals_its_expansion():
                                                   cfg["tree_parent"], SCALE)
     np.testing.assert_allclose(out, bout, rtol=1e-12, atol=1e-14)
     np.testing.assert_allclose(lse, blse, rtol=0, atol=1e-12)
+
+
+# --------------------------------------------------------------------------- ragged trees
+
+def _ragged_case(seed, prefix, tree_lens, heads=2, slots=512, q_scale=1.0):
+    """A packed batch with T_b = tree_lens[b]: every request drawn on its own from the
+    workload recipe, then concatenated (rows, parents, index segments)."""
+    parts = [synth.small_config(seed + 31 * b, batch=1, prefix=[p], tree_nodes=t, heads=heads, slots=slots,
+                                tree="forest" if b % 2 else "random", q_scale=q_scale)
+             for b, (p, t) in enumerate(zip(prefix, tree_lens))]
+    pool = parts[0]["pool"]
+    return dict(q=np.concatenate([c["q"] for c in parts]), pool=pool,
+                kv_indices=np.concatenate([c["kv_indices"] for c in parts]),
+                prefix_lens=np.array(prefix, dtype=np.int32), tree_lens=np.array(tree_lens, dtype=np.int32),
+                tree_parent=np.concatenate([c["tree_parent"][0] for c in parts]), parts=parts)
+
+
+def test_ragged_against_brute_force_per_request():
+    case = _ragged_case(70, [5, 0, 9, 3], [1, 4, 3, 6])
+    out, lse = orc.verify_attention_ragged(case["q"], case["pool"], case["kv_indices"], case["prefix_lens"],
+                                           case["tree_lens"], case["tree_parent"], SCALE)
+    n = 0
+    off = 0
+    for b, c in enumerate(case["parts"]):
+        t, p = int(case["tree_lens"][b]), int(case["prefix_lens"][b])
+        bo, bl = orc.brute_force_verify_attention(c["q"], case["pool"], case["kv_indices"][off:off + p + t],
+                                                  [p], c["tree_parent"], SCALE)
+        np.testing.assert_allclose(out[n:n + t], bo, rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(lse[n:n + t], bl, rtol=0, atol=1e-12)
+        n += t
+        off += p + t
+
+
+def test_ragged_with_equal_trees_is_the_uniform_layout():
+    cfg = synth.small_config(71, batch=3, prefix=[40, 7, 0], tree_nodes=5, heads=3, slots=512, q_scale=1.0)
+    a = orc.verify_attention(cfg["q"], cfg["pool"], cfg["kv_indices"], cfg["prefix_lens"], cfg["tree_parent"], SCALE)
+    b = orc.verify_attention_ragged(cfg["q"], cfg["pool"], cfg["kv_indices"], cfg["prefix_lens"], [5, 5, 5],
+                                    cfg["tree_parent"].reshape(-1), SCALE)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    assert orc.node_offsets([5, 5, 5]).tolist() == [0, 5, 10]
+    assert orc.node_offsets([1, 64, 200, 3]).tolist() == [0, 1, 65, 265]
+
+
+def test_ragged_matches_padding_with_extra_roots():
+    # a 5-node tree padded to 9 nodes with extra roots (their own slots) gives the same rows
+    case = _ragged_case(72, [30], [5])
+    rng = np.random.default_rng(3)
+    pad_slots = np.setdiff1d(np.arange(512), case["kv_indices"])[:4]
+    q_pad = np.concatenate([case["q"], synth.f32_to_bf16_bits(rng.standard_normal((4, 2, 576), dtype=np.float32))])
+    par_pad = np.concatenate([case["tree_parent"], [-1, -1, -1, -1]]).astype(np.int32)
+    idx_pad = np.concatenate([case["kv_indices"], pad_slots]).astype(np.int32)
+    a = orc.verify_attention_ragged(case["q"], case["pool"], case["kv_indices"], case["prefix_lens"], [5],
+                                    case["tree_parent"], SCALE)
+    b = orc.verify_attention(q_pad, case["pool"], idx_pad, case["prefix_lens"], par_pad[None, :], SCALE)
+    np.testing.assert_allclose(a[0], b[0][:5], rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(a[1], b[1][:5], rtol=0, atol=1e-13)
+
+
+def test_ragged_rejects_bad_shapes():
+    case = _ragged_case(73, [3, 4], [2, 3])
+    with pytest.raises(ValueError):
+        orc.verify_attention_ragged(case["q"], case["pool"], case["kv_indices"], case["prefix_lens"], [2, 0],
+                                    case["tree_parent"], SCALE)
+    with pytest.raises(ValueError):
+        orc.verify_attention_ragged(case["q"], case["pool"], case["kv_indices"][:-1], case["prefix_lens"], [2, 3],
+                                    case["tree_parent"], SCALE)

@@ -57,13 +57,15 @@ BF16_QNAN = np.uint16(0x7FC0)
 def f32_to_bf16_bits(x) -> np.ndarray:
     """Round float32 values to bf16 (round to nearest, ties to even); NaN stays a quiet NaN."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    rounded = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    u = x.view(np.uint32)
+    # in 32 bits: for every non-NaN pattern u + 0x8000 stays below 2^32 (the largest finite
+    # values round to infinity, as they should); NaN patterns are replaced below
+    rounded = ((u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)).astype(np.uint16)
     nan = np.isnan(x)
     if nan.any():
-        sign = ((u >> 16) & 0x8000).astype(np.uint16)
+        sign = ((u >> np.uint32(16)) & np.uint32(0x8000)).astype(np.uint16)
         rounded = np.where(nan, sign | BF16_QNAN, rounded)
-    return rounded.astype(np.uint16)
+    return rounded
 
 
 def bf16_bits_to_f32(b) -> np.ndarray:
