@@ -95,19 +95,25 @@ typedef struct mlaverify_config {
 } mlaverify_config;
 
 /* Checks a configuration without touching the GPU.  Returns MLAVERIFY_OK,
- * MLAVERIFY_ERR_INVALID_ARG or MLAVERIFY_ERR_UNSUPPORTED. */
+ * MLAVERIFY_ERR_INVALID_ARG or MLAVERIFY_ERR_UNSUPPORTED.  The limits it checks follow
+ * from the kernels (one rank's heads, up to 256 tree nodes, 32-bit segment offsets); the
+ * pages fix none of them beyond page_size=1 ("Chunk 66.0" summary), which is the default. */
 MLAVERIFY_API int mlaverify_validate_config(const mlaverify_config* cfg);
 
 /* Bytes of device workspace a handle with this configuration needs (0 if the
- * configuration is invalid).  Pure host computation. */
+ * configuration is invalid).  Pure host computation.  The "Chunk 66.1" summary has the
+ * verify kernel run in a torch-allocated workspace with a fixed split count, so that it can
+ * be captured; this is that workspace's size: the split partials (bf16 outputs and fp32
+ * log-sum-exps of every unit) plus small plan, relocation and acceptance areas. */
 MLAVERIFY_API size_t mlaverify_workspace_bytes(const mlaverify_config* cfg);
 
 /* Creates a handle on the current HIP device.  workspace: a device buffer of at
  * least mlaverify_workspace_bytes(cfg) bytes, 256-byte aligned, owned by the
- * caller and kept alive until mlaverify_destroy; or NULL, in which case the
- * library allocates (and later frees) it.  The workspace needs no
- * initialisation; create clears the small error area with a synchronous memset.
- * On success *out receives the handle. */
+ * caller and kept alive until mlaverify_destroy (the caller-provided workspace of the
+ * "Chunk 66.1" summary); or NULL, in which case the library allocates (and later frees)
+ * it.  The workspace needs no initialisation; create clears the small error area with a
+ * synchronous memset, so create itself is not for graph capture.  On success *out
+ * receives the handle; on failure *out is NULL and nothing stays allocated. */
 MLAVERIFY_API int mlaverify_create(const mlaverify_config* cfg, void* workspace,
                                    size_t workspace_bytes, mlaverify_t* out);
 
@@ -238,7 +244,8 @@ MLAVERIFY_API int mlaverify_accept(mlaverify_t h, int32_t batch, int32_t tree_no
                                    const float* logits, const int32_t* draft_tokens, const int32_t* tree_parent,
                                    int32_t* accept_len, int32_t* accepted, int32_t* bonus, void* stream);
 
-/* Builds the tree-ancestor bitmasks alone (the mask step of run, on its own), as
+/* Builds the tree-ancestor bitmasks alone (the mask step of run, on its own; the "Chunk
+ * 66.1" summary times the CPU mask build of its serving stack at 0.18 ms per step), as
  * W = ceil(T / 64) words per node: bit j % 64 of masks[(b*T + i)*W + j / 64] is set iff
  * tree node j is node i or one of its ancestors.
  * tree_parent int32 [batch, T] and masks uint64 [batch, T, W] are device pointers;
@@ -276,11 +283,17 @@ MLAVERIFY_API int mlaverify_probe_gather(const void* kv_pool, int64_t kv_row_str
 MLAVERIFY_API int mlaverify_read_plan(mlaverify_t h, int32_t batch, void* stream, int32_t* host_out,
                                       int32_t capacity);
 
-/* Reads and clears the sticky device-error bits (synchronises `stream`). */
+/* Reads and clears the sticky device-error bits (synchronises `stream`; for tests and
+ * monitoring, not for graphs).  The bits are the data errors the kernels detect instead of
+ * reading out of bounds (MLAVERIFY_DEVERR_*); the pages' kernel is checked for token-exact
+ * agreement with a naive reference ("Chunk 66.0" summary), and these bits are how a run that
+ * could not be exact says so. */
 MLAVERIFY_API int mlaverify_read_device_errors(mlaverify_t h, void* stream, uint32_t* flags);
 
-/* Kernel timing for benchmarks (not for graph capture).  After
- * mlaverify_profile_begin(h, n) the next n calls of mlaverify_run record HIP events
+/* Kernel timing for benchmarks (not for graph capture).  The "Chunk 66.0" summary finds
+ * that the reduction kernel and the tile sizing still needed work; these events time the
+ * partial pass and the merge apart, on the run's own stream.  After
+ * mlaverify_profile_begin(h, n) the next n calls of mlaverify_run (or _ragged) record HIP events
  * on their stream before and after each of their two kernels (partial pass, merge).
  * mlaverify_profile_end synchronises on the last event, writes host_ms[2*i + k] =
  * duration in milliseconds of kernel k of recorded run i for
@@ -289,10 +302,12 @@ MLAVERIFY_API int mlaverify_read_device_errors(mlaverify_t h, void* stream, uint
 MLAVERIFY_API int mlaverify_profile_begin(mlaverify_t h, int32_t max_runs);
 MLAVERIFY_API int mlaverify_profile_end(mlaverify_t h, float* host_ms, int32_t capacity_runs);
 
-/* Releases the handle (and the workspace if the library allocated it). */
+/* Releases the handle (and the workspace if the library allocated it).  The caller must
+ * have finished (synchronised) every call enqueued on it.  Returns MLAVERIFY_ERR_INVALID_ARG
+ * for a NULL handle. */
 MLAVERIFY_API int mlaverify_destroy(mlaverify_t h);
 
-/* Static text for a status code. */
+/* Static text for a status code (never NULL; "unknown status" for codes outside the list). */
 MLAVERIFY_API const char* mlaverify_status_string(int status);
 
 #ifdef __cplusplus

@@ -244,6 +244,44 @@ def check_device_code(src: str, verbose: bool = False) -> None:
             print(f"{n}: scratch {b} B, vgpr+agpr {v}", flush=True)
 
 
+ASAN_LIB_PATH = os.path.join(PKG_DIR, "libmlaverify_asan.so")
+
+
+def asan_runtime() -> str:
+    """clang's shared AddressSanitizer runtime of the ROCm toolchain (preloaded by the ASan tests)."""
+    import glob
+
+    hits = sorted(glob.glob(os.path.join(os.path.dirname(os.path.dirname(hipcc())), "llvm", "lib", "clang", "*", "lib",
+                                         "linux", "libclang_rt.asan-x86_64.so")))
+    if not hits:
+        raise RuntimeError("clang's libclang_rt.asan-x86_64.so not found next to hipcc")
+    return hits[-1]
+
+
+def build_asan(verbose: bool = False) -> str:
+    """The same library with the host code built under AddressSanitizer (device code unchanged), for
+    CPU tests of the C ABI's host paths.  Load it with asan_runtime() preloaded."""
+    build_dir = os.path.join(PKG_DIR, "_build", "asan")
+    os.makedirs(build_dir, exist_ok=True)
+    flags = [f for f in HIPCC_FLAGS if f != "-O3"] + ["-O1", "-g", "-Xarch_host", "-fsanitize=address",
+                                                        "-Xarch_host", "-fno-omit-frame-pointer"]
+    objs, procs = [], []
+    for src in SOURCES:
+        obj = os.path.join(build_dir, src.replace(".hip", ".o"))
+        cmd = [hipcc(), *flags, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
+        procs.append(subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True))
+        objs.append(obj)
+    for p in procs:
+        out, _ = p.communicate()
+        if p.returncode:
+            raise RuntimeError("hipcc (ASan build) failed:\n" + out[-4000:])
+    tmp = ASAN_LIB_PATH + ".tmp"
+    subprocess.run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Xarch_host", "-fsanitize=address",
+                    "-shared-libasan", "-o", tmp, *objs], check=True)
+    os.replace(tmp, ASAN_LIB_PATH)
+    return ASAN_LIB_PATH
+
+
 def build(verbose: bool = False) -> str:
     """Compile every source for gfx950 and link the shared library; returns its path."""
     objs = []
@@ -279,3 +317,5 @@ def build(verbose: bool = False) -> str:
 
 if __name__ == "__main__":
     print(build(verbose="--verbose" in sys.argv))
+    if "--asan" in sys.argv:
+        print(build_asan(verbose="--verbose" in sys.argv))
