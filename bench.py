@@ -8,7 +8,9 @@ kernel's roofline and, unless --no-cpu, the CPU oracle timed on the host.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config 3] [--warm] [--no-cpu]
 
-The default run times the 185k-token workload (the headline line) and then, with the same
+Before the W warmup steps of each workload, the bench runs untimed calls for 0.3 s so that
+the GPU clocks have ramped up (`settle`).  The default run times the 185k-token workload (the
+headline line) and then, with the same
 protocol, every other seeded workload (`per_config`), the measured stream bandwidth of the
 1 GiB flush kernel (`hbm_stream_gbs`, so that %HBM is also given against it) and the
 scattered-read probe on the headline's rows (`gather_probe_gbs`).
@@ -397,7 +399,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=3, help="workload index (workloads.synth.CONFIGS)")
-    ap.add_argument("--variant", default=None, help="workload variant, e.g. contiguous or sorted")
+    ap.add_argument("--variant", default=None,
+                    help="workload variant, e.g. contiguous or sorted, or unit_end_needles (a dominant key at the "
+                         "last prefix key of every split unit)")
     ap.add_argument("--warm", action="store_true", help="do not flush caches between calls")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of the call captured in a HIP graph (the flush stays outside it)")
@@ -493,13 +497,39 @@ PER_CONFIG = [(1, None), (2, None), (2, "sorted"), (2, "contiguous"), (4, None),
 def verify_workload(i: int, variant, page: int):
     from workloads import synth
 
-    cfg = synth.make_config(i, variant=variant)
+    if variant == "unit_end_needles":
+        # a dominant key at the last prefix key of every split unit (the automatic split of
+        # this workload, read back from one call): the worst place for a raised reference
+        cfg = synth.make_config(i)
+        cfg = synth.plant_unit_end_needles(cfg, automatic_split(cfg))
+    else:
+        cfg = synth.make_config(i, variant=variant)
     name = synth.CONFIGS[i]["name"] + (f"+{variant}" if variant else "")
     if page > 1:  # the same shapes with paged prefixes (pages drawn at random, tree slots apart)
         cfg = synth.paged_config(i, batch=cfg["batch"], prefix=[int(p) for p in cfg["prefix_lens"]],
                                  tree_nodes=cfg["tree_nodes"], heads=cfg["heads"], slots=cfg["slots"], page=page)
         name += f"+paged{page}"
     return cfg, name
+
+
+def automatic_split(cfg: dict) -> int:
+    """The split length the library's automatic plan picks for this workload (one call)."""
+    import torch
+
+    import mla_tree_verify_mlaverify_amd as mv
+
+    dev = torch.device("cuda:0")
+
+    def t(a, dt=None):
+        x = torch.from_numpy(np.ascontiguousarray(a if dt is None else a.astype(dt)))
+        return (x.view(torch.int16).view(torch.bfloat16) if dt is None else x).to(dev)
+
+    v = mv.Verifier(num_heads=cfg["heads"], max_batch=cfg["batch"], max_tree_nodes=cfg["tree_nodes"],
+                    max_prefix_len=int(cfg["prefix_lens"].max()), pool_slots=cfg["slots"], sm_scale=cfg["sm_scale"],
+                    device=dev)
+    v.run(t(cfg["q"].view(np.int16)), t(cfg["pool"].view(np.int16)), t(cfg["kv_indices"], np.int32),
+          t(cfg["prefix_lens"], np.int32), t(cfg["tree_parent"], np.int32))
+    return v.read_plan()["split_len"]
 
 
 def stream_bandwidth(flush) -> float:
@@ -515,6 +545,28 @@ def stream_bandwidth(flush) -> float:
     torch.cuda.synchronize()
     ms = statistics.median(a.elapsed_time(b) for a, b in ev[2:])
     return 2 * flush.numel() * 4 / (ms * 1e-3) / 1e9
+
+
+SETTLE_S = 0.3
+
+
+def settle(step, flush, warm: bool) -> None:
+    """Clock settle before the warmup steps: back-to-back calls (with the flush unless warm) for
+    SETTLE_S seconds.  The GPU's clocks take tens of milliseconds of load to ramp up, so with
+    only a few warmup calls the first timed calls ran several percent slower (measured: 185k
+    workload, 5 warmup calls, call median 206.6 µs and p90 224 µs; 40 calls, 195.7 and 196.5)."""
+    import torch
+
+    t0 = time.perf_counter()
+    n = 0
+    while n < 2000 and (n % 8 or time.perf_counter() - t0 < SETTLE_S):
+        if not warm:
+            flush.add_(1.0)
+        step()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
 
 
 def time_verify(cfg: dict, args, flush, steps: int, warmup: int, *, graph: bool, split: int, page: int) -> dict:
@@ -546,6 +598,7 @@ def time_verify(cfg: dict, args, flush, steps: int, warmup: int, *, graph: bool,
     def step():
         v.run(q, pool, kv_idx, plens, par, out=out, lse=lse, stream=stream)
 
+    settle(step, flush, args.warm)
     for _ in range(warmup):
         if not args.warm:
             flush.add_(1.0)
@@ -567,6 +620,7 @@ def time_verify(cfg: dict, args, flush, steps: int, warmup: int, *, graph: bool,
         torch.cuda.synchronize()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    v.read_plan(stream=stream)  # (sets the rescale count back to 0 for the timed calls)
     # Whole calls, timed on their own: the library's per-kernel events (below) would add
     # their own markers between the two launches.
     torch.cuda.synchronize()
@@ -591,6 +645,7 @@ def time_verify(cfg: dict, args, flush, steps: int, warmup: int, *, graph: bool,
     errs = v.read_device_errors()
     assert errs == 0, errs
     plan = v.read_plan()
+    plan["rescales_per_call"] = plan["rescales"] / (2 * steps)
     return dict(call_ms=call_ms, call_ms_median=statistics.median(call_ms), kernel_ms=kernel_ms, plan=plan,
                 wall_s=round(wall, 4))
 
@@ -635,7 +690,8 @@ def verify_summary(cfg: dict, counts: dict, res: dict, copy_gbs: float) -> dict:
         "roofline": roof,
         "plan": {"split_len": s, "total_units": plan["total_units"], "n_mtiles": plan["n_mtiles"],
                  "fast_units": plan["fast_units"], "prefix_units": prefix_units,
-                 "fast_hit_rate": round(plan["fast_units"] / prefix_units, 4) if prefix_units else None},
+                 "fast_hit_rate": round(plan["fast_units"] / prefix_units, 4) if prefix_units else None,
+                 "rescales_per_call": plan["rescales_per_call"]},
     }
 
 

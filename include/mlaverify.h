@@ -270,13 +270,15 @@ MLAVERIFY_API int mlaverify_probe_gather(const void* kv_pool, int64_t kv_row_str
 
 /* Copies the work partition of the most recent run into host memory (synchronises
  * `stream`; for tests and reports, not for graphs).  Writes up to `capacity`
- * int32 values: [split_len, total_units, n_mtiles, fast_units, sclk_khz, then per
- * request b: key_offset_b, prefix_len_b, first_unit_b, units_b, prefix_error_bits_b],
+ * int32 values: [split_len, total_units, n_mtiles, fast_units, sclk_khz, rescales, then
+ * per request b: key_offset_b, prefix_len_b, first_unit_b, units_b, prefix_error_bits_b],
  * where fast_units counts the split units whose prefix slots formed one contiguous run
  * and were read without the index table (the contiguous-run fast path; a unit with no
- * prefix keys never counts), and sclk_khz is the shader clock over the run of the
- * partial kernel's first workgroup (its cycle counter against the device's wall clock;
- * 0 if it was not sampled).  Parent and index errors are reported by
+ * prefix keys never counts), sclk_khz is the shader clock over the run of the partial
+ * kernel's first workgroup (its cycle counter against the device's wall clock; 0 if it
+ * was not sampled), and rescales counts the waves that raised a row's softmax reference
+ * (a tile maximum more than 2^16 above it, which rescales that row's partial sums once)
+ * over every call since the previous readback, which sets it back to 0.  Parent and index errors are reported by
  * mlaverify_read_device_errors only.
  * Returns the number of values available (which may exceed capacity) or a
  * negative status. */

@@ -325,16 +325,16 @@ class Verifier:
     def read_plan(self, batch: int | None = None, stream=None) -> dict:
         """Work partition of the last run (synchronises the stream)."""
         batch = batch or self.last_batch
-        cap = 5 + 5 * batch
+        cap = 6 + 5 * batch
         buf = (ctypes.c_int32 * cap)()
         n = self.lib.mlaverify_read_plan(self.handle, batch, _stream_handle(stream), buf, cap)
         if n < 0:
             raise MlaVerifyError(n, "mlaverify_read_plan")
         vals = list(buf)
-        reqs = [dict(zip(("key_offset", "prefix_len", "first_unit", "units", "error_bits"), vals[5 + 5 * i:10 + 5 * i]))
+        reqs = [dict(zip(("key_offset", "prefix_len", "first_unit", "units", "error_bits"), vals[6 + 5 * i:11 + 5 * i]))
                 for i in range(batch)]
         return dict(split_len=vals[0], total_units=vals[1], n_mtiles=vals[2], fast_units=vals[3],
-                    sclk_mhz=round(vals[4] / 1000.0, 1), requests=reqs)
+                    sclk_mhz=round(vals[4] / 1000.0, 1), rescales=vals[5], requests=reqs)
 
     def profile_begin(self, max_runs: int) -> None:
         """Record HIP events around the kernels of the next max_runs runs."""

@@ -183,6 +183,10 @@ int enqueue_run(const mlaverify_config& c, const RunAreas& w, int batch, int T, 
   ma.H = c.num_heads;
   ma.M = M;
   ma.units_cap = units_grid;
+  // units of one request, as the plan is expected to make them: under an automatic split the
+  // target count shared by the batch (longer requests take more of them, in more rounds)
+  ma.units_hint = c.split_tokens > 0 ? (int)(c.max_prefix_len > 0 ? cdiv(c.max_prefix_len, c.split_tokens) : 1)
+                                     : (int)cdiv(ka.target_units, batch);
 
   const int grid = n_mt * (int)(cdiv(units_grid, 8) * 8);
   if (ev && hipEventRecord(ev[0], s) != hipSuccess) return MLAVERIFY_ERR_HIP;
@@ -445,7 +449,7 @@ int mlaverify_read_plan(mlaverify_t hd, int32_t batch, void* stream, int32_t* ho
   if (!hd || batch < 1 || batch > hd->cfg.max_batch || (capacity > 0 && !host_out) || capacity < 0)
     return MLAVERIFY_ERR_INVALID_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  constexpr int kPlanHead = 5;
+  constexpr int kPlanHead = 6;
   const int needed = kPlanHead + 5 * batch;
   PlanHeader hdr;
   std::vector<ReqPlan> req;
@@ -471,7 +475,12 @@ int mlaverify_read_plan(mlaverify_t hd, int32_t batch, void* stream, int32_t* ho
   if (hipDeviceGetAttribute(&wall_khz, hipDeviceAttributeWallClockRate, hd->device) == hipSuccess && wall_khz > 0 &&
       hdr.clk_ticks > 0)
     sclk_khz = (int32_t)((double)hdr.clk_cycles * wall_khz / hdr.clk_ticks);
-  int32_t vals[kPlanHead] = {hdr.split_len, hdr.total_units, hdr.n_mtiles, fast_units, sclk_khz};
+  // the rescale count runs over every call since the last readback; start it again
+  char* rp = hd->ws + hd->L.hdr + offsetof(PlanHeader, rescales);
+  if (hipMemsetAsync(rp, 0, sizeof(uint32_t), s) != hipSuccess || hipStreamSynchronize(s) != hipSuccess)
+    return MLAVERIFY_ERR_HIP;
+  int32_t vals[kPlanHead] = {hdr.split_len, hdr.total_units, hdr.n_mtiles, fast_units, sclk_khz,
+                             (int32_t)hdr.rescales};
   for (int i = 0; i < kPlanHead && i < capacity; i++) host_out[i] = vals[i];
   for (int b = 0; b < batch; b++) {
     const int32_t rv[5] = {req[b].key_off, req[b].prefix_len, req[b].first_unit, req[b].units, (int32_t)req[b].err};

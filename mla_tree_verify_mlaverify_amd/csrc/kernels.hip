@@ -206,6 +206,39 @@ __device__ __forceinline__ void mfma_acc_v(f32x16& acc, const u32x4& a, const u3
 #define MLV_READ_O_15(X) \
   asm volatile("v_accvgpr_read_b32 %0, a240\n\tv_accvgpr_read_b32 %1, a241\n\tv_accvgpr_read_b32 %2, a242\n\tv_accvgpr_read_b32 %3, a243\n\tv_accvgpr_read_b32 %4, a244\n\tv_accvgpr_read_b32 %5, a245\n\tv_accvgpr_read_b32 %6, a246\n\tv_accvgpr_read_b32 %7, a247\n\tv_accvgpr_read_b32 %8, a248\n\tv_accvgpr_read_b32 %9, a249\n\tv_accvgpr_read_b32 %10, a250\n\tv_accvgpr_read_b32 %11, a251\n\tv_accvgpr_read_b32 %12, a252\n\tv_accvgpr_read_b32 %13, a253\n\tv_accvgpr_read_b32 %14, a254\n\tv_accvgpr_read_b32 %15, a255" : "=v"(X[0]), "=v"(X[1]), "=v"(X[2]), "=v"(X[3]), "=v"(X[4]), "=v"(X[5]), "=v"(X[6]), "=v"(X[7]), "=v"(X[8]), "=v"(X[9]), "=v"(X[10]), "=v"(X[11]), "=v"(X[12]), "=v"(X[13]), "=v"(X[14]), "=v"(X[15]))
 
+#define MLV_WRITE_O_0(X) \
+  asm volatile("v_accvgpr_write_b32 a0, %0\n\tv_accvgpr_write_b32 a1, %1\n\tv_accvgpr_write_b32 a2, %2\n\tv_accvgpr_write_b32 a3, %3\n\tv_accvgpr_write_b32 a4, %4\n\tv_accvgpr_write_b32 a5, %5\n\tv_accvgpr_write_b32 a6, %6\n\tv_accvgpr_write_b32 a7, %7\n\tv_accvgpr_write_b32 a8, %8\n\tv_accvgpr_write_b32 a9, %9\n\tv_accvgpr_write_b32 a10, %10\n\tv_accvgpr_write_b32 a11, %11\n\tv_accvgpr_write_b32 a12, %12\n\tv_accvgpr_write_b32 a13, %13\n\tv_accvgpr_write_b32 a14, %14\n\tv_accvgpr_write_b32 a15, %15" :: "v"(X[0]), "v"(X[1]), "v"(X[2]), "v"(X[3]), "v"(X[4]), "v"(X[5]), "v"(X[6]), "v"(X[7]), "v"(X[8]), "v"(X[9]), "v"(X[10]), "v"(X[11]), "v"(X[12]), "v"(X[13]), "v"(X[14]), "v"(X[15]) : "a0", "a1", "a2", "a3", "a4", "a5", "a6", "a7", "a8", "a9", "a10", "a11", "a12", "a13", "a14", "a15")
+#define MLV_WRITE_O_1(X) \
+  asm volatile("v_accvgpr_write_b32 a16, %0\n\tv_accvgpr_write_b32 a17, %1\n\tv_accvgpr_write_b32 a18, %2\n\tv_accvgpr_write_b32 a19, %3\n\tv_accvgpr_write_b32 a20, %4\n\tv_accvgpr_write_b32 a21, %5\n\tv_accvgpr_write_b32 a22, %6\n\tv_accvgpr_write_b32 a23, %7\n\tv_accvgpr_write_b32 a24, %8\n\tv_accvgpr_write_b32 a25, %9\n\tv_accvgpr_write_b32 a26, %10\n\tv_accvgpr_write_b32 a27, %11\n\tv_accvgpr_write_b32 a28, %12\n\tv_accvgpr_write_b32 a29, %13\n\tv_accvgpr_write_b32 a30, %14\n\tv_accvgpr_write_b32 a31, %15" :: "v"(X[0]), "v"(X[1]), "v"(X[2]), "v"(X[3]), "v"(X[4]), "v"(X[5]), "v"(X[6]), "v"(X[7]), "v"(X[8]), "v"(X[9]), "v"(X[10]), "v"(X[11]), "v"(X[12]), "v"(X[13]), "v"(X[14]), "v"(X[15]) : "a16", "a17", "a18", "a19", "a20", "a21", "a22", "a23", "a24", "a25", "a26", "a27", "a28", "a29", "a30", "a31")
+#define MLV_WRITE_O_2(X) \
+  asm volatile("v_accvgpr_write_b32 a32, %0\n\tv_accvgpr_write_b32 a33, %1\n\tv_accvgpr_write_b32 a34, %2\n\tv_accvgpr_write_b32 a35, %3\n\tv_accvgpr_write_b32 a36, %4\n\tv_accvgpr_write_b32 a37, %5\n\tv_accvgpr_write_b32 a38, %6\n\tv_accvgpr_write_b32 a39, %7\n\tv_accvgpr_write_b32 a40, %8\n\tv_accvgpr_write_b32 a41, %9\n\tv_accvgpr_write_b32 a42, %10\n\tv_accvgpr_write_b32 a43, %11\n\tv_accvgpr_write_b32 a44, %12\n\tv_accvgpr_write_b32 a45, %13\n\tv_accvgpr_write_b32 a46, %14\n\tv_accvgpr_write_b32 a47, %15" :: "v"(X[0]), "v"(X[1]), "v"(X[2]), "v"(X[3]), "v"(X[4]), "v"(X[5]), "v"(X[6]), "v"(X[7]), "v"(X[8]), "v"(X[9]), "v"(X[10]), "v"(X[11]), "v"(X[12]), "v"(X[13]), "v"(X[14]), "v"(X[15]) : "a32", "a33", "a34", "a35", "a36", "a37", "a38", "a39", "a40", "a41", "a42", "a43", "a44", "a45", "a46", "a47")
+#define MLV_WRITE_O_3(X) \
+  asm volatile("v_accvgpr_write_b32 a48, %0\n\tv_accvgpr_write_b32 a49, %1\n\tv_accvgpr_write_b32 a50, %2\n\tv_accvgpr_write_b32 a51, %3\n\tv_accvgpr_write_b32 a52, %4\n\tv_accvgpr_write_b32 a53, %5\n\tv_accvgpr_write_b32 a54, %6\n\tv_accvgpr_write_b32 a55, %7\n\tv_accvgpr_write_b32 a56, %8\n\tv_accvgpr_write_b32 a57, %9\n\tv_accvgpr_write_b32 a58, %10\n\tv_accvgpr_write_b32 a59, %11\n\tv_accvgpr_write_b32 a60, %12\n\tv_accvgpr_write_b32 a61, %13\n\tv_accvgpr_write_b32 a62, %14\n\tv_accvgpr_write_b32 a63, %15" :: "v"(X[0]), "v"(X[1]), "v"(X[2]), "v"(X[3]), "v"(X[4]), "v"(X[5]), "v"(X[6]), "v"(X[7]), "v"(X[8]), "v"(X[9]), "v"(X[10]), "v"(X[11]), "v"(X[12]), "v"(X[13]), "v"(X[14]), "v"(X[15]) : "a48", "a49", "a50", "a51", "a52", "a53", "a54", "a55", "a56", "a57", "a58", "a59", "a60", "a61", "a62", "a63")
+#define MLV_WRITE_O_4(X) \
+  asm volatile("v_accvgpr_write_b32 a64, %0\n\tv_accvgpr_write_b32 a65, %1\n\tv_accvgpr_write_b32 a66, %2\n\tv_accvgpr_write_b32 a67, %3\n\tv_accvgpr_write_b32 a68, %4\n\tv_accvgpr_write_b32 a69, %5\n\tv_accvgpr_write_b32 a70, %6\n\tv_accvgpr_write_b32 a71, %7\n\tv_accvgpr_write_b32 a72, %8\n\tv_accvgpr_write_b32 a73, %9\n\tv_accvgpr_write_b32 a74, %10\n\tv_accvgpr_write_b32 a75, %11\n\tv_accvgpr_write_b32 a76, %12\n\tv_accvgpr_write_b32 a77, %13\n\tv_accvgpr_write_b32 a78, %14\n\tv_accvgpr_write_b32 a79, %15" :: "v"(X[0]), "v"(X[1]), "v"(X[2]), "v"(X[3]), "v"(X[4]), "v"(X[5]), "v"(X[6]), "v"(X[7]), "v"(X[8]), "v"(X[9]), "v"(X[10]), "v"(X[11]), "v"(X[12]), "v"(X[13]), "v"(X[14]), "v"(X[15]) : "a64", "a65", "a66", "a67", "a68", "a69", "a70", "a71", "a72", "a73", "a74", "a75", "a76", "a77", "a78", "a79")
+#define MLV_WRITE_O_5(X) \
+  asm volatile("v_accvgpr_write_b32 a80, %0\n\tv_accvgpr_write_b32 a81, %1\n\tv_accvgpr_write_b32 a82, %2\n\tv_accvgpr_write_b32 a83, %3\n\tv_accvgpr_write_b32 a84, %4\n\tv_accvgpr_write_b32 a85, %5\n\tv_accvgpr_write_b32 a86, %6\n\tv_accvgpr_write_b32 a87, %7\n\tv_accvgpr_write_b32 a88, %8\n\tv_accvgpr_write_b32 a89, %9\n\tv_accvgpr_write_b32 a90, %10\n\tv_accvgpr_write_b32 a91, %11\n\tv_accvgpr_write_b32 a92, %12\n\tv_accvgpr_write_b32 a93, %13\n\tv_accvgpr_write_b32 a94, %14\n\tv_accvgpr_write_b32 a95, %15" :: "v"(X[0]), "v"(X[1]), "v"(X[2]), "v"(X[3]), "v"(X[4]), "v"(X[5]), "v"(X[6]), "v"(X[7]), "v"(X[8]), "v"(X[9]), "v"(X[10]), "v"(X[11]), "v"(X[12]), "v"(X[13]), "v"(X[14]), "v"(X[15]) : "a80", "a81", "a82", "a83", "a84", "a85", "a86", "a87", "a88", "a89", "a90", "a91", "a92", "a93", "a94", "a95")
+#define MLV_WRITE_O_6(X) \
+  asm volatile("v_accvgpr_write_b32 a96, %0\n\tv_accvgpr_write_b32 a97, %1\n\tv_accvgpr_write_b32 a98, %2\n\tv_accvgpr_write_b32 a99, %3\n\tv_accvgpr_write_b32 a100, %4\n\tv_accvgpr_write_b32 a101, %5\n\tv_accvgpr_write_b32 a102, %6\n\tv_accvgpr_write_b32 a103, %7\n\tv_accvgpr_write_b32 a104, %8\n\tv_accvgpr_write_b32 a105, %9\n\tv_accvgpr_write_b32 a106, %10\n\tv_accvgpr_write_b32 a107, %11\n\tv_accvgpr_write_b32 a108, %12\n\tv_accvgpr_write_b32 a109, %13\n\tv_accvgpr_write_b32 a110, %14\n\tv_accvgpr_write_b32 a111, %15" :: "v"(X[0]), "v"(X[1]), "v"(X[2]), "v"(X[3]), "v"(X[4]), "v"(X[5]), "v"(X[6]), "v"(X[7]), "v"(X[8]), "v"(X[9]), "v"(X[10]), "v"(X[11]), "v"(X[12]), "v"(X[13]), "v"(X[14]), "v"(X[15]) : "a96", "a97", "a98", "a99", "a100", "a101", "a102", "a103", "a104", "a105", "a106", "a107", "a108", "a109", "a110", "a111")
+#define MLV_WRITE_O_7(X) \
+  asm volatile("v_accvgpr_write_b32 a112, %0\n\tv_accvgpr_write_b32 a113, %1\n\tv_accvgpr_write_b32 a114, %2\n\tv_accvgpr_write_b32 a115, %3\n\tv_accvgpr_write_b32 a116, %4\n\tv_accvgpr_write_b32 a117, %5\n\tv_accvgpr_write_b32 a118, %6\n\tv_accvgpr_write_b32 a119, %7\n\tv_accvgpr_write_b32 a120, %8\n\tv_accvgpr_write_b32 a121, %9\n\tv_accvgpr_write_b32 a122, %10\n\tv_accvgpr_write_b32 a123, %11\n\tv_accvgpr_write_b32 a124, %12\n\tv_accvgpr_write_b32 a125, %13\n\tv_accvgpr_write_b32 a126, %14\n\tv_accvgpr_write_b32 a127, %15" :: "v"(X[0]), "v"(X[1]), "v"(X[2]), "v"(X[3]), "v"(X[4]), "v"(X[5]), "v"(X[6]), "v"(X[7]), "v"(X[8]), "v"(X[9]), "v"(X[10]), "v"(X[11]), "v"(X[12]), "v"(X[13]), "v"(X[14]), "v"(X[15]) : "a112", "a113", "a114", "a115", "a116", "a117", "a118", "a119", "a120", "a121", "a122", "a123", "a124", "a125", "a126", "a127")
+#define MLV_WRITE_O_8(X) \
+  asm volatile("v_accvgpr_write_b32 a128, %0\n\tv_accvgpr_write_b32 a129, %1\n\tv_accvgpr_write_b32 a130, %2\n\tv_accvgpr_write_b32 a131, %3\n\tv_accvgpr_write_b32 a132, %4\n\tv_accvgpr_write_b32 a133, %5\n\tv_accvgpr_write_b32 a134, %6\n\tv_accvgpr_write_b32 a135, %7\n\tv_accvgpr_write_b32 a136, %8\n\tv_accvgpr_write_b32 a137, %9\n\tv_accvgpr_write_b32 a138, %10\n\tv_accvgpr_write_b32 a139, %11\n\tv_accvgpr_write_b32 a140, %12\n\tv_accvgpr_write_b32 a141, %13\n\tv_accvgpr_write_b32 a142, %14\n\tv_accvgpr_write_b32 a143, %15" :: "v"(X[0]), "v"(X[1]), "v"(X[2]), "v"(X[3]), "v"(X[4]), "v"(X[5]), "v"(X[6]), "v"(X[7]), "v"(X[8]), "v"(X[9]), "v"(X[10]), "v"(X[11]), "v"(X[12]), "v"(X[13]), "v"(X[14]), "v"(X[15]) : "a128", "a129", "a130", "a131", "a132", "a133", "a134", "a135", "a136", "a137", "a138", "a139", "a140", "a141", "a142", "a143")
+#define MLV_WRITE_O_9(X) \
+  asm volatile("v_accvgpr_write_b32 a144, %0\n\tv_accvgpr_write_b32 a145, %1\n\tv_accvgpr_write_b32 a146, %2\n\tv_accvgpr_write_b32 a147, %3\n\tv_accvgpr_write_b32 a148, %4\n\tv_accvgpr_write_b32 a149, %5\n\tv_accvgpr_write_b32 a150, %6\n\tv_accvgpr_write_b32 a151, %7\n\tv_accvgpr_write_b32 a152, %8\n\tv_accvgpr_write_b32 a153, %9\n\tv_accvgpr_write_b32 a154, %10\n\tv_accvgpr_write_b32 a155, %11\n\tv_accvgpr_write_b32 a156, %12\n\tv_accvgpr_write_b32 a157, %13\n\tv_accvgpr_write_b32 a158, %14\n\tv_accvgpr_write_b32 a159, %15" :: "v"(X[0]), "v"(X[1]), "v"(X[2]), "v"(X[3]), "v"(X[4]), "v"(X[5]), "v"(X[6]), "v"(X[7]), "v"(X[8]), "v"(X[9]), "v"(X[10]), "v"(X[11]), "v"(X[12]), "v"(X[13]), "v"(X[14]), "v"(X[15]) : "a144", "a145", "a146", "a147", "a148", "a149", "a150", "a151", "a152", "a153", "a154", "a155", "a156", "a157", "a158", "a159")
+#define MLV_WRITE_O_10(X) \
+  asm volatile("v_accvgpr_write_b32 a160, %0\n\tv_accvgpr_write_b32 a161, %1\n\tv_accvgpr_write_b32 a162, %2\n\tv_accvgpr_write_b32 a163, %3\n\tv_accvgpr_write_b32 a164, %4\n\tv_accvgpr_write_b32 a165, %5\n\tv_accvgpr_write_b32 a166, %6\n\tv_accvgpr_write_b32 a167, %7\n\tv_accvgpr_write_b32 a168, %8\n\tv_accvgpr_write_b32 a169, %9\n\tv_accvgpr_write_b32 a170, %10\n\tv_accvgpr_write_b32 a171, %11\n\tv_accvgpr_write_b32 a172, %12\n\tv_accvgpr_write_b32 a173, %13\n\tv_accvgpr_write_b32 a174, %14\n\tv_accvgpr_write_b32 a175, %15" :: "v"(X[0]), "v"(X[1]), "v"(X[2]), "v"(X[3]), "v"(X[4]), "v"(X[5]), "v"(X[6]), "v"(X[7]), "v"(X[8]), "v"(X[9]), "v"(X[10]), "v"(X[11]), "v"(X[12]), "v"(X[13]), "v"(X[14]), "v"(X[15]) : "a160", "a161", "a162", "a163", "a164", "a165", "a166", "a167", "a168", "a169", "a170", "a171", "a172", "a173", "a174", "a175")
+#define MLV_WRITE_O_11(X) \
+  asm volatile("v_accvgpr_write_b32 a176, %0\n\tv_accvgpr_write_b32 a177, %1\n\tv_accvgpr_write_b32 a178, %2\n\tv_accvgpr_write_b32 a179, %3\n\tv_accvgpr_write_b32 a180, %4\n\tv_accvgpr_write_b32 a181, %5\n\tv_accvgpr_write_b32 a182, %6\n\tv_accvgpr_write_b32 a183, %7\n\tv_accvgpr_write_b32 a184, %8\n\tv_accvgpr_write_b32 a185, %9\n\tv_accvgpr_write_b32 a186, %10\n\tv_accvgpr_write_b32 a187, %11\n\tv_accvgpr_write_b32 a188, %12\n\tv_accvgpr_write_b32 a189, %13\n\tv_accvgpr_write_b32 a190, %14\n\tv_accvgpr_write_b32 a191, %15" :: "v"(X[0]), "v"(X[1]), "v"(X[2]), "v"(X[3]), "v"(X[4]), "v"(X[5]), "v"(X[6]), "v"(X[7]), "v"(X[8]), "v"(X[9]), "v"(X[10]), "v"(X[11]), "v"(X[12]), "v"(X[13]), "v"(X[14]), "v"(X[15]) : "a176", "a177", "a178", "a179", "a180", "a181", "a182", "a183", "a184", "a185", "a186", "a187", "a188", "a189", "a190", "a191")
+#define MLV_WRITE_O_12(X) \
+  asm volatile("v_accvgpr_write_b32 a192, %0\n\tv_accvgpr_write_b32 a193, %1\n\tv_accvgpr_write_b32 a194, %2\n\tv_accvgpr_write_b32 a195, %3\n\tv_accvgpr_write_b32 a196, %4\n\tv_accvgpr_write_b32 a197, %5\n\tv_accvgpr_write_b32 a198, %6\n\tv_accvgpr_write_b32 a199, %7\n\tv_accvgpr_write_b32 a200, %8\n\tv_accvgpr_write_b32 a201, %9\n\tv_accvgpr_write_b32 a202, %10\n\tv_accvgpr_write_b32 a203, %11\n\tv_accvgpr_write_b32 a204, %12\n\tv_accvgpr_write_b32 a205, %13\n\tv_accvgpr_write_b32 a206, %14\n\tv_accvgpr_write_b32 a207, %15" :: "v"(X[0]), "v"(X[1]), "v"(X[2]), "v"(X[3]), "v"(X[4]), "v"(X[5]), "v"(X[6]), "v"(X[7]), "v"(X[8]), "v"(X[9]), "v"(X[10]), "v"(X[11]), "v"(X[12]), "v"(X[13]), "v"(X[14]), "v"(X[15]) : "a192", "a193", "a194", "a195", "a196", "a197", "a198", "a199", "a200", "a201", "a202", "a203", "a204", "a205", "a206", "a207")
+#define MLV_WRITE_O_13(X) \
+  asm volatile("v_accvgpr_write_b32 a208, %0\n\tv_accvgpr_write_b32 a209, %1\n\tv_accvgpr_write_b32 a210, %2\n\tv_accvgpr_write_b32 a211, %3\n\tv_accvgpr_write_b32 a212, %4\n\tv_accvgpr_write_b32 a213, %5\n\tv_accvgpr_write_b32 a214, %6\n\tv_accvgpr_write_b32 a215, %7\n\tv_accvgpr_write_b32 a216, %8\n\tv_accvgpr_write_b32 a217, %9\n\tv_accvgpr_write_b32 a218, %10\n\tv_accvgpr_write_b32 a219, %11\n\tv_accvgpr_write_b32 a220, %12\n\tv_accvgpr_write_b32 a221, %13\n\tv_accvgpr_write_b32 a222, %14\n\tv_accvgpr_write_b32 a223, %15" :: "v"(X[0]), "v"(X[1]), "v"(X[2]), "v"(X[3]), "v"(X[4]), "v"(X[5]), "v"(X[6]), "v"(X[7]), "v"(X[8]), "v"(X[9]), "v"(X[10]), "v"(X[11]), "v"(X[12]), "v"(X[13]), "v"(X[14]), "v"(X[15]) : "a208", "a209", "a210", "a211", "a212", "a213", "a214", "a215", "a216", "a217", "a218", "a219", "a220", "a221", "a222", "a223")
+#define MLV_WRITE_O_14(X) \
+  asm volatile("v_accvgpr_write_b32 a224, %0\n\tv_accvgpr_write_b32 a225, %1\n\tv_accvgpr_write_b32 a226, %2\n\tv_accvgpr_write_b32 a227, %3\n\tv_accvgpr_write_b32 a228, %4\n\tv_accvgpr_write_b32 a229, %5\n\tv_accvgpr_write_b32 a230, %6\n\tv_accvgpr_write_b32 a231, %7\n\tv_accvgpr_write_b32 a232, %8\n\tv_accvgpr_write_b32 a233, %9\n\tv_accvgpr_write_b32 a234, %10\n\tv_accvgpr_write_b32 a235, %11\n\tv_accvgpr_write_b32 a236, %12\n\tv_accvgpr_write_b32 a237, %13\n\tv_accvgpr_write_b32 a238, %14\n\tv_accvgpr_write_b32 a239, %15" :: "v"(X[0]), "v"(X[1]), "v"(X[2]), "v"(X[3]), "v"(X[4]), "v"(X[5]), "v"(X[6]), "v"(X[7]), "v"(X[8]), "v"(X[9]), "v"(X[10]), "v"(X[11]), "v"(X[12]), "v"(X[13]), "v"(X[14]), "v"(X[15]) : "a224", "a225", "a226", "a227", "a228", "a229", "a230", "a231", "a232", "a233", "a234", "a235", "a236", "a237", "a238", "a239")
+#define MLV_WRITE_O_15(X) \
+  asm volatile("v_accvgpr_write_b32 a240, %0\n\tv_accvgpr_write_b32 a241, %1\n\tv_accvgpr_write_b32 a242, %2\n\tv_accvgpr_write_b32 a243, %3\n\tv_accvgpr_write_b32 a244, %4\n\tv_accvgpr_write_b32 a245, %5\n\tv_accvgpr_write_b32 a246, %6\n\tv_accvgpr_write_b32 a247, %7\n\tv_accvgpr_write_b32 a248, %8\n\tv_accvgpr_write_b32 a249, %9\n\tv_accvgpr_write_b32 a250, %10\n\tv_accvgpr_write_b32 a251, %11\n\tv_accvgpr_write_b32 a252, %12\n\tv_accvgpr_write_b32 a253, %13\n\tv_accvgpr_write_b32 a254, %14\n\tv_accvgpr_write_b32 a255, %15" :: "v"(X[0]), "v"(X[1]), "v"(X[2]), "v"(X[3]), "v"(X[4]), "v"(X[5]), "v"(X[6]), "v"(X[7]), "v"(X[8]), "v"(X[9]), "v"(X[10]), "v"(X[11]), "v"(X[12]), "v"(X[13]), "v"(X[14]), "v"(X[15]) : "a240", "a241", "a242", "a243", "a244", "a245", "a246", "a247", "a248", "a249", "a250", "a251", "a252", "a253", "a254", "a255")
+
 __device__ __forceinline__ void pv_mfma(int db, const u32x4& v, const u32x4& p) {
   switch (db) {
     case 0: MLV_PV_MFMA_0(v, p); break;
@@ -461,27 +494,24 @@ __device__ int plan_units(const PartialArgs& a, int g, bool publish, int* s_tmp,
 }
 
 // Gathers of a unit with at most 64 rows in one M tile, run by waves 2 and 3, which hold
-// no rows, so that the compute waves issue none after tiles 0 and 1.  Rows pass through these waves' VGPRs
-// (plain non-temporal 16-byte loads, which reach a higher rate from HBM than LDS-DMA
-// gathers) on their way to LDS.  Helper thread hh covers keys hk and hk + 16 of a tile and
-// chunk slot hc of each of the 9 groups.  Two register stages hold tiles t+2 and t+3:
-// each tile's loads go out two iterations before it is written to LDS, so that two tiles
-// are in flight.  The loop mirrors the compute waves' barriers one for one from their
-// first scores on: that barrier, one per iteration, another on a restart (after the first
-// gathers again), and the final OR.  The function is kept out of line so that nothing of
-// the compute path is live in it.  Its arguments are scalars passed by value: a field read
-// through a reference is a flat load, whose waits would drain the stages, and a struct
-// passed by value goes through the stack (private scratch).  pidx / tidx are the prefix and
-// tree parts of the unit's index segment, as in the kernel.
+// no rows, so that the compute waves issue none after tiles 0 and 1.  Rows pass through
+// these waves' VGPRs (plain non-temporal 16-byte loads, which reach a higher rate from HBM
+// than LDS-DMA gathers) on their way to LDS.  Helper thread hh covers keys hk and hk + 16 of
+// a tile and chunk slot hc of each of the 9 groups.  Two register stages hold tiles t+2 and
+// t+3: each tile's loads go out two iterations before it is written to LDS, so that two
+// tiles are in flight.  The loop mirrors the compute waves' barriers one for one from their
+// first scores on: that barrier, one per iteration, and the final OR.  The function is
+// inlined behind a marker that the build's register audit knows (these waves may use the
+// AGPRs, the compute waves may not); it never returns, the waves end in it.  pidx / tidx are
+// the prefix and tree parts of the unit's index segment, as in the kernel.
 template <bool kPaged>
 [[noreturn]] __device__ __attribute__((always_inline)) inline void gather_helper(const char* pool_in, int64_t row_stride_bytes,
                                                         int64_t pool_slots, int T, int page_log2, int max_page,
                                                         const int32_t* pidx, const int32_t* tidx, int kbeg, int npk,
                                                         int npt, int ntiles, int run_base, int bad_index,
-                                                        char* smem, int* s_restart_in) {
+                                                        char* smem) {
   typedef __attribute__((address_space(1))) const char gmem_char;
   gmem_char* pool = (gmem_char*)pool_in;
-  int (*s_restart)[kWaves] = reinterpret_cast<int (*)[kWaves]>(s_restart_in);
   typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
   lds_char* lds = (lds_char*)smem;
   const int tid = threadIdx.x;
@@ -512,24 +542,6 @@ template <bool kPaged>
     const bool oob = (uint32_t)idx >= (uint64_t)pool_slots;
     bad |= oob ? 1 : 0;
     return (const char*)(pool + (uint64_t)(oob ? 0u : (uint32_t)idx) * (uint64_t)row_stride_bytes);
-  };
-  // The first gathers of a pass, as every thread issues them: key tid / 8 of tiles 0 and 1.
-  auto dma_tiles01 = [&]() {
-    const int kt = tid >> 3;
-    const int kx = (tid & 7) ^ swz(kt);
-    for (int tl = 0; tl < 2 && tl < ntiles; tl++) {
-      const char* src = row_of(slot_of(tl, index_of(tl, kt), kt)) + kx * 16;
-      const uint32_t d = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds + tl * kTileBytes) + wu * 1024);
-      lds_dma16<0>(src, d);
-      lds_dma16<1>(src, d);
-      lds_dma16<2>(src, d);
-      lds_dma16<3>(src, d);
-      lds_dma16<4>(src, d);
-      lds_dma16<5>(src, d);
-      lds_dma16<6>(src, d);
-      lds_dma16<7>(src, d);
-      lds_dma16<8>(src, d);
-    }
   };
   auto tile0_barrier = [&]() {  // start_scores: tile 0 has landed everywhere
     if (ntiles > 1) {
@@ -583,40 +595,25 @@ template <bool kPaged>
     rows(st, tl + 4, en);
     entries(en, tl + 6);
   };
-  // The loop top: 0 = go on with tile t, 1 = the pass is over, 2 = it starts again.
-  int t = 0;
-  auto top = [&]() -> int {
+  // The loop mirrors the compute waves' barriers: the first scores', then one per tile until
+  // the last.  It is unrolled by two, one stage per half, so that every path into its head
+  // leaves the loads in the same order (st0, en0, st1, en1) and the compiler's waits stay
+  // counted.
+  tile0_barrier();
+  start();
+  for (int t = 0;;) {
     __syncthreads();
-    const int* fl = s_restart[(t - 1) & 1];
-    if (t > 0 && (fl[0] | fl[1] | fl[2] | fl[3]) != 0) return 2;
-    return t == ntiles ? 1 : 0;
-  };
-  // One pass per outer iteration (a restart gathers tiles 0 and 1 again first).  The inner
-  // loop is unrolled by two, one stage per half, so that every path into its head leaves
-  // the loads in the same order (st0, en0, st1, en1) and the compiler's waits stay counted.
-  for (bool first = true;; first = false) {
-    if (!first) dma_tiles01();
-    tile0_barrier();
-    start();
-    t = 0;
-    int c;
-    for (;;) {
-      if ((c = top()) != 0) break;
-      step(st0, en0, t);
-      s_restart[t & 1][wu] = 0;
-      t++;
-      if ((c = top()) != 0) break;
-      step(st1, en1, t);
-      s_restart[t & 1][wu] = 0;
-      t++;
-    }
-    if (c == 1) break;
+    if (t == ntiles) break;
+    step(st0, en0, t);
+    t++;
+    __syncthreads();
+    if (t == ntiles) break;
+    step(st1, en1, t);
+    t++;
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // no load in flight when the workgroup ends
   (void)__syncthreads_or(bad);         // the epilogue's
-  // The helper waves end here.  Never returning also spares the call its callee-saved
-  // register spills (the waves hold nothing the kernel would need afterwards).
-  __builtin_amdgcn_endpgm();
+  __builtin_amdgcn_endpgm();           // the helper waves end here
 }
 
 // kPaged: the prefix is addressed through a block table of 2^page_log2-slot pages (the
@@ -628,7 +625,6 @@ template <bool kPaged, bool kBigTree, bool kHelp>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_partial(PartialArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[kTileBufs * kTileBytes + kWaves * kQLdsBytes];
-  __shared__ int s_restart[2][kWaves];
   __shared__ int s_tmp[kWaves];
   __shared__ int s_unit[10];
   lds_char* lds = (lds_char*)smem;
@@ -847,11 +843,11 @@ void k_partial(PartialArgs a) {
       }
   }
 
-  // Softmax state of row lrow (log2 domain).  mref is a fixed reference for the whole
-  // pass over the unit: it is set by the first tile in which the row sees a key, and every
-  // later probability 2^(s - mref) is kept <= 2^16.  A tile whose maximum exceeds mref by
-  // more than 16 raises mref and restarts the unit (rare: it needs a score jump of > 11
-  // nats after the first tile), so the output accumulator is never rescaled.
+  // Softmax state of row lrow (log2 domain).  mref is the row's reference: it is set by the
+  // first tile in which the row sees a key, and every probability 2^(s - mref) is kept
+  // <= 2^16.  A tile whose maximum exceeds mref by more than 16 raises mref to that maximum
+  // and scales the row's accumulator and sum by 2^(old - new) once (rare: it needs a score
+  // jump of more than 11 nats after the row's first keys), so the common path never rescales.
   const float c2 = a.scale_log2;  // > 0
   float mref = -INFINITY;
   float lrun = 0.f;
@@ -877,7 +873,7 @@ void k_partial(PartialArgs a) {
   // next tile so that the VALU work runs while the matrix core is busy.  Each probability
   // is packed as soon as its pair is complete, so few of them are live at once.  No maximum
   // is taken here: a probability above 2^16 shows in the lane's sum, and only then (rarely)
-  // is the tile's maximum computed, for the reference test (see `restart_test`).
+  // is the tile's maximum computed (raise_reference).
   auto soft_step = [&](Soft& o, const f32x16& sc, float nm, int i) {
     if (i < 16) {
       const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], c2, nm));
@@ -887,23 +883,6 @@ void k_partial(PartialArgs a) {
       else
         o.pe = e;
     }
-  };
-  // After the softmax of tile t (scores sc): if some row's tile maximum exceeds its reference
-  // by more than 16 (log2 units), raise the reference to it and flag the wave, so that every
-  // wave restarts the unit at the next barrier.  A lane's sum of 16 probabilities exceeds
-  // 2^16 whenever one of them does, so the maximum is only needed when a sum does.
-  auto restart_test = [&](const f32x16& sc, float psum) -> bool {
-    bool trig = false;
-    if (__builtin_expect(__any(psum > 65536.0f), 0)) {
-      float m = sc[0];
-#pragma unroll
-      for (int v = 1; v < 16; v++) m = fmaxf(m, sc[v]);
-      const float tmax = xhalf_max(m) * c2;
-      const bool raise = mref != -INFINITY && tmax > mref + 16.0f;
-      trig = __any(raise);
-      if (raise) mref = tmax;  // the pass is abandoned at the next barrier; keep the larger reference
-    }
-    return trig;
   };
 
   // One chain of 36 score MFMAs over the tile at kb.  Optionally interleaves the softmax
@@ -1010,6 +989,45 @@ void k_partial(PartialArgs a) {
     }
   };
 
+  // Scale this lane's part of the output accumulator (256 values of its row) by f.
+  auto scale_o = [&](float f) __attribute__((always_inline)) {
+    asm volatile("s_nop 15\n\ts_nop 3" ::: "memory");  // every PV MFMA has written the accumulator
+    float X[16];
+#define MLV_SCALE_BLOCK(N)                                  \
+  MLV_READ_O_##N(X);                                        \
+  _Pragma("unroll") for (int k = 0; k < 16; k++) X[k] *= f; \
+  MLV_WRITE_O_##N(X);
+    MLV_SCALE_BLOCK(0) MLV_SCALE_BLOCK(1) MLV_SCALE_BLOCK(2) MLV_SCALE_BLOCK(3)
+    MLV_SCALE_BLOCK(4) MLV_SCALE_BLOCK(5) MLV_SCALE_BLOCK(6) MLV_SCALE_BLOCK(7)
+    MLV_SCALE_BLOCK(8) MLV_SCALE_BLOCK(9) MLV_SCALE_BLOCK(10) MLV_SCALE_BLOCK(11)
+    MLV_SCALE_BLOCK(12) MLV_SCALE_BLOCK(13) MLV_SCALE_BLOCK(14) MLV_SCALE_BLOCK(15)
+#undef MLV_SCALE_BLOCK
+    asm volatile("s_nop 1" ::: "memory");  // the accumulator writes before its next MFMA use
+  };
+  // After the softmax of tile t (scores sc, probabilities so against mref): a lane's sum of
+  // 16 probabilities exceeds 2^16 whenever one of them does, so only then (rarely) is the
+  // tile's maximum taken.  Rows whose maximum exceeds mref by more than 16 raise mref to it
+  // and scale their accumulator and running sum by 2^(old - new); the tile's probabilities
+  // are then computed again against the new reference.
+  auto raise_reference = [&](const f32x16& sc, Soft& so) {
+    if (__builtin_expect(__any(so.psum > 65536.0f), 0)) {
+      float m = sc[0];
+#pragma unroll
+      for (int v = 1; v < 16; v++) m = fmaxf(m, sc[v]);
+      const float tmax = xhalf_max(m) * c2;
+      const bool raise = mref != -INFINITY && tmax > mref + 16.0f;
+      if (__any(raise)) {
+        if (lane == 0) atomicAdd(&a.hdr->rescales, 1u);
+        const float f = raise ? __builtin_amdgcn_exp2f(mref - tmax) : 1.0f;
+        scale_o(f);
+        lrun *= f;
+        if (raise) mref = tmax;
+#pragma unroll
+        for (int i = 0; i < 16; i++) soft_step(so, sc, -mref, i);
+      }
+    }
+  };
+
   // Software pipeline over the tiles of the unit, three LDS buffers in rotation (tile t in
   // buffer bi).  Iteration t, after the barrier that makes tile t+1 visible: the deferred PV
   // blocks of tile t-1, then S(t+1) on the matrix core with the softmax of tile t in its gaps
@@ -1020,10 +1038,10 @@ void k_partial(PartialArgs a) {
   f32x16 sacc;       // S^T of tile t
   Soft dummy_soft;
   const f32x16 zero16 = {};
-  // First half of a pass: the gathers of tiles 0 and 1.  The index entries of tiles 0..2
-  // were loaded before (the first pass: in the prologue; a restart: just before), and all
-  // three have landed before any gather goes out, since the compiler cannot see a gather's
-  // completion and a wait for an index issued after one would also wait for it.
+  // First the gathers of tiles 0 and 1.  The index entries of tiles 0..2 were loaded in the
+  // prologue, and all three have landed before any gather goes out, since the compiler
+  // cannot see a gather's completion and a wait for an index issued after one would also
+  // wait for it.
   auto start_gathers = [&](int e0, int e1, int e2) {
     t = 0;
     bi = 0;
@@ -1037,7 +1055,7 @@ void k_partial(PartialArgs a) {
     issue_tile(0, src0);
     if (ntiles > 1) issue_tile(1, src1);
   };
-  // Second half: once tile 0 has landed everywhere, its scores.
+  // Then, once tile 0 has landed everywhere, its scores.
   auto start_scores = [&]() {
     if (ntiles > 1) {
       __builtin_amdgcn_s_waitcnt(0x0F79);  // vmcnt(9): tile 0 landed (tile 1 may not)
@@ -1080,36 +1098,30 @@ void k_partial(PartialArgs a) {
       asm volatile("; mlv-helper-waves" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);  // keep the helper's code below the marker
       gather_helper<kPaged>(reinterpret_cast<const char*>(a.pool), a.row_stride_bytes, a.pool_slots, Tb,
-                            a.page_log2, a.max_page, pidx, tidx, kbeg, npk, npt, ntiles, run_base, bad_index, smem,
-                            &s_restart[0][0]);
+                            a.page_log2, a.max_page, pidx, tidx, kbeg, npk, npt, ntiles, run_base, bad_index, smem);
       return;
     }
   }
   start_scores();
-  // Deferred PV fragments and their P operand; zero before a pass's first tile, so that the
-  // deferred MFMAs at its first barrier add nothing.
+  // Deferred PV fragments and their P operand; zero before the first tile, so that the
+  // deferred MFMAs at the first barrier add nothing.
   u32x4 vdef[kDeferArr][2], pdef[2];
-  auto clear_deferred = [&]() {
 #pragma unroll
-    for (int k = 0; k < kDeferArr; k++) vdef[k][0] = vdef[k][1] = u32x4{0u, 0u, 0u, 0u};
-    pdef[0] = pdef[1] = u32x4{0u, 0u, 0u, 0u};
-  };
-  clear_deferred();
+  for (int k = 0; k < kDeferArr; k++) vdef[k][0] = vdef[k][1] = u32x4{0u, 0u, 0u, 0u};
+  pdef[0] = pdef[1] = u32x4{0u, 0u, 0u, 0u};
   // Tiles t with t + 3 < nfull (all of t .. t+3 are full prefix tiles) take the steady body:
   // no tail or tree masks, no clamped keys, no first-reference step.
   const int nfull = npk / kTileKeys;
-  // One iteration; returns 0 to go on, 1 at the end of the unit, 2 for a restart.
+  // One iteration; returns 0 to go on, 1 at the end of the unit.
   auto iteration = [&](auto steady) -> int {
     constexpr bool kSteady = decltype(steady)::value != 0;
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's loads of tile t+1 landed
     __syncthreads();                     // ... and everyone's; PV(t-1) finished everywhere
-    // Reads that need only the barrier go out first (the restart flags of tile t-1 and the
-    // first fragments of S(t+1)); the deferred PV MFMAs of tile t-1 cover their latency.
+    // The first fragments of S(t+1) need only the barrier; the deferred PV MFMAs of tile t-1
+    // cover their latency.
     const int b1 = bi == kTileBufs - 1 ? 0 : bi + 1;
     const int b2 = b1 == kTileBufs - 1 ? 0 : b1 + 1;
     const lds_char* kb1 = lds + b1 * kTileBytes;
-    const int* fl = s_restart[(t - 1) & 1];
-    const int flags = fl[0] | fl[1] | fl[2] | fl[3];
     const SPre pre = s_pre(kb1);
     pv_deferred(vdef, pdef);
     // Gathers of tile t+2 go to buffer b2 (on the last tiles they re-read pool row 0 into it;
@@ -1126,11 +1138,8 @@ void k_partial(PartialArgs a) {
       }
       pf_dst = tile_dst(b2);
     }
-    const bool prev_flags = t > 0 && flags != 0;  // some wave raised its reference at tile t-1
-    if (kSteady) {
-      if (__builtin_expect(prev_flags, 0)) return 2;
-    } else {
-      if (__builtin_expect(t == ntiles || prev_flags, 0)) return prev_flags ? 2 : 1;
+    if (!kSteady) {
+      if (__builtin_expect(t == ntiles, 0)) return 1;
       // Tail and tree tiles: invisible keys get -inf (key of register v is 4h + 8(v/4) + v%4).
       const bool tree = t >= npt;
       const int tt = t - npt;
@@ -1177,7 +1186,7 @@ void k_partial(PartialArgs a) {
     const lds_char* kb = lds + bi * kTileBytes;
     u32x4 vc0[2];
     load_v(kb, 0, vc0);
-    s_restart[t & 1][w] = restart_test(sacc, so.psum) ? 1 : 0;
+    raise_reference(sacc, so);
     lrun += so.psum;
     pv_head(kb, so.pb, vc0, vdef);
     pdef[0] = so.pb[0];
@@ -1187,24 +1196,13 @@ void k_partial(PartialArgs a) {
     t++;
     return 0;
   };
-  for (;;) {
-    int c;
-    do {
-      if (t + 3 < nfull && !need_init)
-        c = iteration(IntC<1>{});
-      else
-        c = iteration(IntC<0>{});
-    } while (c == 0);
-    if (c == 1) break;
-    // the pass starts over with the raised references
-    asm volatile("s_nop 15\n\ts_nop 3" ::: "memory");  // PV MFMAs of the last tile have landed
-    MLV_ZERO_O();
-    lrun = 0.f;
-    clear_deferred();
-    const int e0 = load_index(0), e1 = ntiles > 1 ? load_index(1) : 0, e2 = ntiles > 2 ? load_index(2) : 0;
-    start_gathers(e0, e1, e2);
-    start_scores();
+  for (int c = 0; c == 0;) {
+    if (t + 3 < nfull && !need_init)
+      c = iteration(IntC<1>{});
+    else
+      c = iteration(IntC<0>{});
   }
+  // (the iteration that found the end ran the last tile's deferred PV blocks at its top)
 
   asm volatile("s_nop 15\n\ts_nop 3" ::: "memory");  // last PV MFMA results settle before reads
   if (bid == 0 && wu == 0) {
@@ -1275,14 +1273,14 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
 
 // Row a.6.  kSplit workgroups per output row, each over kCols = 512/kSplit of its columns,
 // so that the grid fills the chip even when there are few rows.  Every lane loads kPer
-// columns of a unit's partial: a group of kCols/kPer lanes covers one unit, so a wave takes
-// 64/(kCols/kPer) units at once and the workgroup kSlots = 4 * that many (slot s: units s,
-// s + kSlots, ...).  With few rows (kSplit = 8) lanes load 16 bytes and a wave takes 8
-// units; otherwise a wave covers the workgroup's columns and takes one unit.  The workgroup first finds m = max_u lse_u (all threads loading
-// at once); then each slot sums its units in steps of kMergeDepth, all of a step's loads in
-// flight, and the slots add up through LDS in a fixed order.
-// A NaN partial lse (a poisoned unit) makes the row NaN.
-template <int kSplit, int kPer>
+// columns (16 bytes) of a unit's partial: a group of kCols/kPer lanes covers one unit, so a
+// wave takes 64/(kCols/kPer) units at once and the workgroup kSlots = 4 * that many (slot s:
+// units s, s + kSlots, ...).  Each slot loads up to kDepth of its units' lses and partials in
+// one round, all in flight together, so that a row costs one memory round trip (rows with
+// more units than kSlots * kDepth take further rounds, folded in by an online rescale).  The
+// round's maximum lse, taken over the workgroup, is the reference of the weights; the slots
+// add up through LDS in a fixed order.  A NaN partial lse (a poisoned unit) makes the row NaN.
+template <int kSplit, int kPer, int kDepth>
 __global__ __launch_bounds__(256) void k_merge(MergeArgs a) {
   constexpr int kCols = kVdim / kSplit;   // columns of this workgroup
   constexpr int kLanes = kCols / kPer;    // lanes per unit
@@ -1306,49 +1304,39 @@ __global__ __launch_bounds__(256) void k_merge(MergeArgs a) {
   const float* pl = a.part_lse + (size_t)R.first_unit * a.M + r;
   const uint16_t* pob = a.part_o + ((size_t)R.first_unit * a.M + r) * kVdim + c0 + kPer * cl;
   const size_t ustride = (size_t)a.M * kVdim;
-  // Reference m = max_u lse_u, with all 256 threads loading the unit lses at once.
-  float m = -INFINITY;
-  for (int u = tid; u < R.units; u += kThreads) m = fmaxf(m, pl[(size_t)u * a.M]);
-  m = wave_max(m);
-  if (lane == 0) s_m[w] = m;
-  __syncthreads();
-  m = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
-  float z = 0.f;
+  float m = -INFINITY, z = 0.f;
   fv acc = {};
-  // One step: kMergeDepth units of this slot, all loads before any use so that no wait
-  // lands between them.  Only the last step of a slot can run past its last unit.  With
-  // several units per wave, that step re-reads the last unit in place of the missing ones
-  // (no branch between the loads) and drops them; with one, the rest go one unit at a
-  // time, which measured faster there.
-  auto step = [&](int u0, auto pred) {
-    constexpr bool kPred = decltype(pred)::value != 0;
-    float lu[kMergeDepth];
-    hv o[kMergeDepth];
+  for (int k0 = slot; k0 - slot < R.units; k0 += kDepth * kSlots) {  // rounds (uniform over the workgroup)
+    float lu[kDepth];
+    hv o[kDepth];
+    // every load of the round before any use; units past the last re-read it and are dropped
 #pragma unroll
-    for (int k = 0; k < kMergeDepth; k++) {
-      const int u = kPred ? min(u0 + k * kSlots, R.units - 1) : u0 + k * kSlots;
+    for (int k = 0; k < kDepth; k++) {
+      const int u = min(k0 + k * kSlots, R.units - 1);
       lu[k] = pl[(size_t)u * a.M];
       o[k] = *reinterpret_cast<const hv*>(pob + u * ustride);
     }
+    float mr = -INFINITY;
 #pragma unroll
-    for (int k = 0; k < kMergeDepth; k++) {
-      const bool live = !kPred || u0 + k * kSlots < R.units;
-      const float wt = (!live || lu[k] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(lu[k] - m);
-      const fv ov = __builtin_convertvector(o[k], fv);
-      z += wt;
-      acc += live ? wt * ov : fv{};
+    for (int k = 0; k < kDepth; k++)
+      if (k0 + k * kSlots < R.units) mr = fmaxf(mr, lu[k]);
+    mr = wave_max(mr);
+    if (lane == 0) s_m[w] = mr;
+    __syncthreads();
+    mr = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
+    __syncthreads();  // s_m is rewritten by the next round
+    if (mr > m) {  // a larger reference: rescale what the earlier rounds summed
+      const float f = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mr);
+      z *= f;
+      acc *= f;
+      m = mr;
     }
-  };
-  int u0 = slot;
-  for (; u0 + (kMergeDepth - 1) * kSlots < R.units; u0 += kMergeDepth * kSlots) step(u0, IntC<0>{});
-  if constexpr (kGroups > 1) {
-    if (u0 < R.units) step(u0, IntC<1>{});
-  } else {
-    for (; u0 < R.units; u0 += kSlots) {
-      const float lu = pl[(size_t)u0 * a.M];
-      const float wt = (lu == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(lu - m);
+#pragma unroll
+    for (int k = 0; k < kDepth; k++) {
+      const bool live = k0 + k * kSlots < R.units;
+      const float wt = (!live || lu[k] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(lu[k] - m);
       z += wt;
-      acc += wt * __builtin_convertvector(*reinterpret_cast<const hv*>(pob + u0 * ustride), fv);
+      acc += live ? wt * __builtin_convertvector(o[k], fv) : fv{};
     }
   }
   *reinterpret_cast<fv*>(&s_acc[slot][kPer * cl]) = acc;
@@ -1359,14 +1347,14 @@ __global__ __launch_bounds__(256) void k_merge(MergeArgs a) {
   for (int q = 0; q < kSlots; q++) Z += s_z[q];
   const float inv = 1.0f / Z;
   for (int c = 2 * tid; c < kCols; c += 2 * kThreads) {
-    float o[2] = {0.f, 0.f};
+    float o2[2] = {0.f, 0.f};
 #pragma unroll
     for (int q = 0; q < kSlots; q++) {
-      o[0] += s_acc[q][c];
-      o[1] += s_acc[q][c + 1];
+      o2[0] += s_acc[q][c];
+      o2[1] += s_acc[q][c + 1];
     }
     reinterpret_cast<uint32_t*>(a.out + orow * kVdim + c0 + c)[0] =
-        bf16_rne_bits(o[0] * inv) | (bf16_rne_bits(o[1] * inv) << 16);
+        bf16_rne_bits(o2[0] * inv) | (bf16_rne_bits(o2[1] * inv) << 16);
   }
   if (c0 == 0 && tid == 0) a.lse[orow] = (m + __builtin_amdgcn_logf(Z)) * 0.69314718055994531f;
 }
@@ -1390,15 +1378,29 @@ hipError_t launch_partial(const PartialArgs& a, int grid, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int kSplit>
+static void launch_merge_split(const MergeArgs& a, int rows, hipStream_t s) {
+  // kDepth: the smallest of 2, 4, 8 units per slot that holds the launch's units in one round
+  constexpr int kSlots = kWaves * 64 / (kVdim / kSplit / 8);
+  const int depth = a.units_hint <= 2 * kSlots ? 2 : a.units_hint <= 4 * kSlots ? 4 : 8;
+  if (depth == 2)
+    hipLaunchKernelGGL((k_merge<kSplit, 8, 2>), dim3(rows * kSplit), dim3(256), 0, s, a);
+  else if (depth == 4)
+    hipLaunchKernelGGL((k_merge<kSplit, 8, 4>), dim3(rows * kSplit), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_merge<kSplit, 8, 8>), dim3(rows * kSplit), dim3(256), 0, s, a);
+}
+
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
-  // about kMergeBlocks workgroups: up to 8 per row when rows are few, whole rows when many
+  // about kMergeBlocks workgroups: up to 8 per row when rows are few, whole rows when many;
+  // 16-byte lanes throughout
   const int rows = a.batch * a.M;
   const int split = rows * 8 <= kMergeBlocks ? 8 : rows * 4 <= kMergeBlocks ? 4 : rows * 2 <= kMergeBlocks ? 2 : 1;
   switch (split) {
-    case 8: hipLaunchKernelGGL((k_merge<8, 8>), dim3(rows * 8), dim3(256), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((k_merge<4, 2>), dim3(rows * 4), dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((k_merge<2, 4>), dim3(rows * 2), dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL((k_merge<1, 8>), dim3(rows), dim3(256), 0, s, a); break;
+    case 8: launch_merge_split<8>(a, rows, s); break;
+    case 4: launch_merge_split<4>(a, rows, s); break;
+    case 2: launch_merge_split<2>(a, rows, s); break;
+    default: launch_merge_split<1>(a, rows, s); break;
   }
   return hipGetLastError();
 }

@@ -17,7 +17,6 @@ constexpr int kWaves = 4;
 constexpr int kRowsPerBlock = kRowsPerWave * kWaves;  // 128 rows per workgroup (M tile)
 constexpr int kThreads = 64 * kWaves;
 constexpr int kQReg = 24;                               // Q k-steps (16 columns each) kept in VGPRs
-constexpr int kMergeDepth = 8;                        // partial loads in flight per merge wave
 constexpr int kMergeBlocks = 2048;                     // merge grid target: rows x column split
 constexpr int kTileBufs = 3;                           // KV tiles in LDS: tile t, t+1 (in use), t+2 (landing)
 constexpr int kQLdsBytes = (36 - kQReg) * 64 * 16;      // per-wave LDS slice for the other k-steps
@@ -46,7 +45,8 @@ struct PlanHeader {
   uint32_t sticky_err;   // OR of every data error since the last readback
   uint32_t clk_cycles;   // shader-clock cycles of workgroup 0's first wave over its run (0: not sampled)
   uint32_t clk_ticks;    // constant-rate wall-clock ticks over the same interval
-  uint32_t pad1[57];     // header is 256 bytes
+  uint32_t rescales;     // waves that raised a softmax reference, since the last plan readback
+  uint32_t pad1[56];     // header is 256 bytes
 };
 static_assert(sizeof(PlanHeader) == 256, "header size");
 
@@ -93,6 +93,7 @@ struct MergeArgs {
   uint16_t* out;
   float* lse;
   int32_t batch, H, M, units_cap;  // M = H * (the call's largest T): the partials' row stride
+  int32_t units_hint;              // units of one request the plan is expected to make (sizes the merge's rounds)
 };
 
 // Tier-1 relocation of prefix rows (relocate.hip).

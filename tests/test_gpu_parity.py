@@ -221,6 +221,28 @@ def test_ragged_trees_by_padding():
     compare(out, lse, ref_out, ref_lse)
 
 
+@pytest.mark.parametrize("cfg_i,split", [(1, 256), (0, 96), (2, 0)])
+def test_reference_raised_at_every_unit_end(cfg_i, split):
+    """A dominant key at the last prefix key of every unit: every row's softmax reference is
+    raised in the last prefix tile of each unit, where the rows' partial sums are rescaled
+    once.  Matches the oracle; the plan readback counts the waves that rescaled."""
+    cfg = synth.make_config(cfg_i)
+    v = verifier_for(cfg, split_tokens=split)
+    run_gpu(cfg, v)
+    plan = v.read_plan()  # the split the automatic plan chooses (and a fresh rescale count)
+    s = plan["split_len"]
+    planted = synth.plant_unit_end_needles(cfg, s)
+    out, lse, _ = run_gpu(planted, v)
+    plan = v.read_plan()
+    assert plan["split_len"] == s
+    prefix_units = sum(min(r["units"], -(-r["prefix_len"] // s)) for r in plan["requests"])
+    waves = -(-cfg["heads"] * cfg["tree_nodes"] // 32)  # waves holding rows, over all M tiles
+    assert plan["rescales"] >= prefix_units - 1 and plan["rescales"] <= prefix_units * waves, plan["rescales"]
+    ref_out, ref_lse = run_oracle(planted)
+    assert np.abs(ref_out).max() > 1.0  # the needles dominate
+    print(compare(out, lse, ref_out, ref_lse))
+
+
 def test_q_zero_lse_is_log_count():
     cfg = synth.make_config(0, variant="qzero")
     out, lse, _ = run_gpu(cfg)

@@ -290,6 +290,29 @@ VARIANTS = ("sorted", "contiguous", "poison_unused", "sharp", "qzero", "needle_p
             "needle_tree", "prefix0", "chain", "colscale")
 
 
+def plant_unit_end_needles(cfg: dict, split: int, seed: int = 0) -> dict:
+    """Plant a dominant key (as in the needle variants) at the last prefix key of every split
+    unit of ``split`` tokens: prefix positions min(P_b, (u + 1) * split) - 1 of each request.
+    Every row then meets a key far above its running maximum in the last prefix tile of each
+    unit, the worst place for a raised softmax reference."""
+    rng = np.random.default_rng(2000 + seed)
+    u = np.where(rng.integers(0, 2, size=LATENT_DIM) == 1, 1.0, -1.0).astype(np.float32)
+    cfg = dict(cfg)
+    pool = cfg["pool"].copy()
+    offs = request_offsets(cfg["prefix_lens"], cfg["tree_nodes"])
+    needles = []
+    for b, o in enumerate(offs):
+        p = int(cfg["prefix_lens"][b])
+        for end in range(split, p + split, split):
+            slot = int(cfg["kv_indices"][int(o) + min(p, end) - 1])
+            pool[slot, :LATENT_DIM] = f32_to_bf16_bits(2.0 * u)
+            needles.append(slot)
+    cfg["q"] = f32_to_bf16_bits(bf16_bits_to_f32(cfg["q"]) + 0.5 * u[None, None, :])
+    cfg["pool"] = pool
+    cfg["needle_slots"] = np.array(needles, dtype=np.int64)
+    return cfg
+
+
 def apply_variant(cfg: dict, variant: str, rng: np.random.Generator | None = None) -> dict:
     """Apply one named transformation (see ``VARIANTS``) to a config built by ``make_config``."""
     cfg = dict(cfg)
