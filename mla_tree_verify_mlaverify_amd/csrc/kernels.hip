@@ -318,7 +318,7 @@ __device__ int wg_exclusive_scan(int v, int* s_tmp, int& total) {
 // node offset) and returns the number of units.  The publishing workgroup also writes the
 // plan out.
 struct UnitPlan {
-  int b, key_off, prefix, first, units, split;
+  int b, key_off, prefix, first, units, split, tree_nodes, node_off, total;
   uint32_t err;
 };
 
@@ -493,6 +493,93 @@ __device__ int plan_units(const PartialArgs& a, int g, bool publish, int* s_tmp,
   return total_units;
 }
 
+// Inclusive scan of one int per lane over the wave (row shifts within each 16-lane row, then
+// the row totals carried across rows; lanes with no source add 0).  Every lane must be active.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
+  return x;
+}
+
+// The same partition for a batch of at most 64 requests, computed by each wave on its own
+// (lane i holds request i) with wave-wide scans: no LDS and no barrier.  Returns false,
+// uniformly over the workgroup, when the batch needs plan_units instead: more than 64
+// requests, or ragged requests whose unit count rounds past the target (the split search).
+// Fills up for unit g; a publishing wave writes the plan out.
+__device__ bool plan_wave(const PartialArgs& a, int g, bool publish, UnitPlan& up) {
+  const int B = a.batch, T = a.T;
+  if (B > 64) return false;
+  const int lane = threadIdx.x & 63;
+  const bool in = lane < B;
+  int pv = a.prefix_lens[min(lane, B - 1)];
+  int tl = a.tree_lens ? a.tree_lens[min(lane, B - 1)] : T;
+  const int bp = (in && (pv < 0 || pv > a.max_prefix)) ? 1 : 0;
+  const int bt = (in && (tl < 1 || tl > T)) ? 1 : 0;
+  const int run_bad = wave_incl_scan(bp + (bt << 16));  // bad prefix lengths low, tree lengths high
+  const uint32_t err = ((run_bad & 0xFFFF) ? kErrBadPrefix : 0u) | ((run_bad >> 16) ? kErrBadTreeLen : 0u);
+  if (!in || err) pv = 0;
+  if (!in || (err & kErrBadTreeLen)) tl = 0;
+  const bool fixed_split = a.split_fixed > 0;
+  const int tk = fixed_split ? 0 : (tl + kTileKeys - 1) / kTileKeys * kTileKeys;
+  const int seg = in ? seg_entries(pv, a.page_log2) + tl : 0;
+  const int seg_inc = wave_incl_scan(seg);
+  const int node_inc = wave_incl_scan(tl);
+  int S = a.split_fixed;
+  if (!fixed_split) {
+    const int work = __builtin_amdgcn_readlane(wave_incl_scan(pv + tk), 63);
+    const int U = a.target_units;
+    S = max(a.min_split, ((work + U - 1) / U + kTileKeys - 1) / kTileKeys * kTileKeys);
+  }
+  const int units = in ? max(1, min((pv + tk + S - 1) / S, (pv + S - 1) / S + 1)) : 0;
+  const int first_inc = wave_incl_scan(units);
+  const int total = __builtin_amdgcn_readlane(first_inc, 63);
+  if (!fixed_split && total > a.target_units && B < a.target_units) return false;
+  const int first = first_inc - units;
+  const uint64_t mine = __ballot(in && g >= first && g < first_inc);
+  up.split = S;
+  up.total = total;
+  if (mine) {
+    const int l = __builtin_ctzll(mine);
+    up.b = l;
+    up.key_off = __builtin_amdgcn_readlane(seg_inc - seg, l);
+    up.prefix = __builtin_amdgcn_readlane(pv, l);
+    up.first = __builtin_amdgcn_readlane(first, l);
+    up.units = __builtin_amdgcn_readlane(units, l);
+    up.err = (uint32_t)__builtin_amdgcn_readlane((int)err, l);
+    up.tree_nodes = __builtin_amdgcn_readlane(tl, l);
+    up.node_off = __builtin_amdgcn_readlane(node_inc - tl, l);
+  } else {
+    up.b = up.key_off = up.prefix = up.first = up.units = up.tree_nodes = up.node_off = 0;
+    up.err = 0;
+  }
+  if (publish) {
+    if (in) {
+      ReqPlan rp;
+      rp.key_off = seg_inc - seg;
+      rp.prefix_len = pv;
+      rp.first_unit = first;
+      rp.units = units;
+      rp.err = err;
+      rp.tree_nodes = tl;
+      rp.node_off = node_inc - tl;
+      rp.pad = 0;
+      a.req[lane] = rp;
+    }
+    if (lane == 0) {
+      a.hdr->split_len = S;
+      a.hdr->total_units = total;
+      a.hdr->n_mtiles = a.n_mtiles;
+      const int tot_bad = __builtin_amdgcn_readlane(run_bad, 63);
+      if (tot_bad) atomicOr(a.sticky_err, ((tot_bad & 0xFFFF) ? kErrBadPrefix : 0u) | ((tot_bad >> 16) ? kErrBadTreeLen : 0u));
+    }
+  }
+  return true;
+}
+
 // Gathers of a unit with at most 64 rows in one M tile, run by waves 2 and 3, which hold
 // no rows, so that the compute waves issue none after tiles 0 and 1.  Rows pass through
 // these waves' VGPRs (plain non-temporal 16-byte loads, which reach a higher rate from HBM
@@ -516,7 +603,6 @@ template <bool kPaged>
   lds_char* lds = (lds_char*)smem;
   const int tid = threadIdx.x;
   const int hh = tid - 2 * 64, hk = hh >> 3, hc = hh & 7;
-  const uint32_t wu = __builtin_amdgcn_readfirstlane(tid >> 6);
   int bad = bad_index;
   const int pmask = (1 << page_log2) - 1;
   auto page_slot = [&](int e, int pos) -> int {
@@ -657,17 +743,28 @@ void k_partial(PartialArgs a) {
     rt0 = __builtin_amdgcn_s_memrealtime();
   }
   // (tile buffer 0 is the plan's scratch: no gather writes it before the plan is done)
-  const int total_units = plan_units(a, g, g == 0 && mt == 0, s_tmp, s_unit, reinterpret_cast<int*>(smem));
-  if (g >= total_units || g >= a.units_cap) return;
-  const int b = s_unit[0];
-  const int key_off = s_unit[1];
-  const int prefix = s_unit[2];
-  const int first_unit = s_unit[3];
-  const int nunits = s_unit[4];
-  uint32_t req_err = (uint32_t)s_unit[5];
-  const int S = s_unit[6];
-  const int Tb = s_unit[7];        // this request's tree nodes (the call's T unless ragged)
-  const int node_off = s_unit[8];  // its first row (node) in q / out / tree_parent
+  UnitPlan up;
+  if (!plan_wave(a, g, g == 0 && mt == 0 && wu == 0, up)) {
+    up.total = plan_units(a, g, g == 0 && mt == 0, s_tmp, s_unit, reinterpret_cast<int*>(smem));
+    up.b = s_unit[0];
+    up.key_off = s_unit[1];
+    up.prefix = s_unit[2];
+    up.first = s_unit[3];
+    up.units = s_unit[4];
+    up.err = (uint32_t)s_unit[5];
+    up.split = s_unit[6];
+    up.tree_nodes = s_unit[7];
+    up.node_off = s_unit[8];
+  }
+  if (g >= up.total || g >= a.units_cap) return;
+  const int key_off = up.key_off;
+  const int prefix = up.prefix;
+  const int first_unit = up.first;
+  const int nunits = up.units;
+  uint32_t req_err = up.err;
+  const int S = up.split;
+  const int Tb = up.tree_nodes;      // this request's tree nodes (the call's T unless ragged)
+  const int node_off = up.node_off;  // its first row (node) in q / out / tree_parent
   const int Mb = a.H * Tb;         // its query rows
   const int u = g - first_unit;
   const int kbeg = u * S;
@@ -760,10 +857,10 @@ void k_partial(PartialArgs a) {
     return;
   }
   // Reads that depend only on the plan go out together: the run check's first keys, the
-  // index entries of tiles 0..2 and the tree parents.  Q follows the first gathers (loads
-  // complete in issue order, and the compiler's waits before the gathers cover every load
-  // issued so far), so its latency overlaps theirs.  A poisoned request's segment offsets
-  // are unknown, so nothing is read from its index segment.
+  // index entries of tiles 0..2, the tree parents and then Q, so that Q's latency overlaps
+  // the run check and the first gathers (loads complete in issue order: the waits for the
+  // index entries leave Q in flight).  A poisoned request's segment offsets are unknown, so
+  // nothing is read from its index segment.
   const bool plan_ok = req_err == 0;
   const bool check_run = plan_ok && !(a.flags & 1u) && npk > 0;
   int run_first = 0, run_mine = 0;
@@ -779,6 +876,19 @@ void k_partial(PartialArgs a) {
   }
   int par_i = 0;
   if (last && tid < Tb) par_i = a.tree_parent[(size_t)node_off + tid];
+  // B operand of the score MFMA: Q[row][16kk + 8h .. +7] (bf16 pairs).  Row r of the request
+  // is (node r / H, head r % H).  The first kQReg k-steps stay in VGPRs for the whole unit;
+  // the rest (loaded first) are parked in this wave's LDS slice once they land.  Rows past
+  // M (last M tile) read the request's last row; their results are dropped.
+  u32x4 qf[kQReg], qt[36 - kQReg];
+  if (plan_ok) {
+    const u32x4* qp =
+        reinterpret_cast<const u32x4*>(a.q + ((size_t)node_off * a.H + (rvalid ? r : Mb - 1)) * kLatent) + h;
+#pragma unroll
+    for (int kk = kQReg; kk < 36; kk++) qt[kk - kQReg] = qp[2 * kk];
+#pragma unroll
+    for (int kk = 0; kk < kQReg; kk++) qf[kk] = qp[2 * kk];
+  }
   int* s_jump = reinterpret_cast<int*>(smem + 2 * kTileBytes + kMaxTree * kMaxTreeWords * 8);
   auto masks = [&]() {
     if (build_masks<kW>(par_i, Tb, s_m, s_jump)) {
@@ -818,7 +928,6 @@ void k_partial(PartialArgs a) {
   }
   if (tid == 0 && mt == 0) a.unit_fast[g] = run_base >= 0 ? 1 : 0;  // for the plan readback
   uint64_t anc[kW];  // this row's ancestor-mask words (filled before the first scores)
-  u32x4 qf[kQReg];   // Q k-steps kept in VGPRs (filled after the first gathers)
   typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
   lds_u32x4* qlds = (lds_u32x4*)(lds + kTileBufs * kTileBytes + w * kQLdsBytes) + lane;
 
@@ -1066,29 +1175,16 @@ void k_partial(PartialArgs a) {
     need_init = __any(mref == -INFINITY);
     sacc = s_chain(IntC<-1>{}, IntC<0>{}, lds, nullptr, 0u, zero16, 0.f, dummy_soft, s_pre(lds));
   };
-  MLV_ZERO_O();  // O^T[d = 32db + ..][row] accumulates in a[0..255]
   start_gathers(raw0, raw1, raw2);
-  // B operand of the score MFMA: Q[row][16kk + 8h .. +7] (bf16 pairs).  Row r of the request
-  // is (node r / H, head r % H).  The first kQReg k-steps stay in VGPRs for the whole unit;
-  // the rest are parked in this wave's LDS slice (lane-major, conflict-free).
-  {
-    u32x4 qt[36 - kQReg];
-    // rows past M (last M tile) read the request's last row; their results are dropped
-    const u32x4* qp =
-        reinterpret_cast<const u32x4*>(a.q + ((size_t)node_off * a.H + (rvalid ? r : Mb - 1)) * kLatent) + h;
-#pragma unroll
-    for (int kk = 0; kk < kQReg; kk++) qf[kk] = qp[2 * kk];
-#pragma unroll
-    for (int kk = kQReg; kk < 36; kk++) qt[kk - kQReg] = qp[2 * kk];
-    if (last) masks();
-    if (req_err) {  // a bad parent: the tiles' gathers must land before the workgroup ends
-      __builtin_amdgcn_s_waitcnt(0x0F70);
-      poison();
-      return;
-    }
-#pragma unroll
-    for (int kk = kQReg; kk < 36; kk++) qlds[(kk - kQReg) * 64] = qt[kk - kQReg];
+  MLV_ZERO_O();  // O^T[d = 32db + ..][row] accumulates in a[0..255]
+  if (last) masks();
+  if (req_err) {  // a bad parent: the tiles' gathers must land before the workgroup ends
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    poison();
+    return;
   }
+#pragma unroll
+  for (int kk = kQReg; kk < 36; kk++) qlds[(kk - kQReg) * 64] = qt[kk - kQReg];  // lane-major, conflict-free
 #pragma unroll
   for (int w = 0; w < kW; w++) anc[w] = (last && rvalid) ? s_m[(r / a.H) * kW + w] : ~0ull;
   if constexpr (kHelp) {
