@@ -706,8 +706,12 @@ template <bool kPaged>
 // index segment holds page ids); otherwise through one slot per token.  kBigTree: T > 64,
 // so a row's ancestor mask takes kMaxTreeWords 64-bit words instead of one.  kHelp: at
 // most 64 rows in one M tile, so waves 2 and 3 hold no rows; they gather the tiles
-// (gather_helper) and the compute waves issue none after tiles 0 and 1.
-template <bool kPaged, bool kBigTree, bool kHelp>
+// (gather_helper) and the compute waves issue none after tiles 0 and 1.  kRG: one M tile of
+// more rows; no other workgroup reads the same keys, so every gather goes to HBM, and the
+// compute waves stage their pieces in VGPRs (plain non-temporal 16-byte loads, which reach a
+// higher rate from HBM than direct-to-LDS loads) and write them to LDS at the end of the
+// iteration; the loop then has one body, which leaves the registers for the stage.
+template <bool kPaged, bool kBigTree, bool kHelp, bool kRG>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_partial(PartialArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[kTileBufs * kTileBytes + kWaves * kQLdsBytes];
@@ -996,12 +1000,12 @@ void k_partial(PartialArgs a) {
 
   // One chain of 36 score MFMAs over the tile at kb.  Optionally interleaves the softmax
   // steps of the previous tile (sc -> so) and this wave's 9 gather pieces of a later tile,
-  // one after MFMA number W of every group of four.  (Giving each wave its own W spreads the
-  // pieces over time, but four copies of the chain cost more in instruction fetch and
-  // registers than the address unit's queueing they avoid.)  K fragments are read kSDist
-  // k-steps ahead through a ring of registers; the caller reads the first kSDist of them
-  // (s_pre) as early as the tile is known to be in LDS.
+  // one after each of the first 9 MFMAs, so that the gathers have as much of the iteration
+  // as possible to land (wc >= 0; the helper waves' tiles take none).  K fragments are read
+  // kSDist k-steps ahead through a ring of registers; the caller reads the first kSDist of
+  // them (s_pre) as early as the tile is known to be in LDS.
   constexpr int kSDist = 2;
+  u32x4 rg[kRG ? 9 : 1];  // kRG: this thread's 9 pieces of tile t+2 on their way to LDS
   struct SPre {
     u32x4 k[kSDist], q[kSDist];
   };
@@ -1035,7 +1039,12 @@ void k_partial(PartialArgs a) {
         mfma_first_v(acc, kr[0], qr[0]);
       else
         mfma_acc_v(acc, kr[i % (kSDist + 1)], qr[i % (kSDist + 1)]);
-      if (W >= 0 && (i & 3) == W) issue_piece(psrc, pdst, i >> 2);
+      if (W >= 0 && i < 9) {
+        if constexpr (kRG)
+          rg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(psrc + 128 * i));
+        else
+          issue_piece(psrc, pdst, i);
+      }
       if (kSoft) {
         soft_step(so, sc, nm, i);
         __builtin_amdgcn_sched_barrier(0);
@@ -1287,16 +1296,27 @@ void k_partial(PartialArgs a) {
     pv_head(kb, so.pb, vc0, vdef);
     pdef[0] = so.pb[0];
     pdef[1] = so.pb[1];
+    if constexpr (kRG) {  // tile t+2 into buffer b2 (tile t-1's, which no one reads any more)
+      if (kSteady || t + 1 < ntiles) {
+        lds_u32x4* d = reinterpret_cast<lds_u32x4*>(lds + b2 * kTileBytes) + tid;
+#pragma unroll
+        for (int j = 0; j < 9; j++) d[j * 256] = rg[j];
+      }
+    }
     sacc = snext;
     bi = b1;
     t++;
     return 0;
   };
-  for (int c = 0; c == 0;) {
-    if (t + 3 < nfull && !need_init)
-      c = iteration(IntC<1>{});
-    else
-      c = iteration(IntC<0>{});
+  if constexpr (kRG) {
+    for (int c = 0; c == 0;) c = iteration(IntC<0>{});
+  } else {
+    for (int c = 0; c == 0;) {
+      if (t + 3 < nfull && !need_init)
+        c = iteration(IntC<1>{});
+      else
+        c = iteration(IntC<0>{});
+    }
   }
   // (the iteration that found the end ran the last tile's deferred PV blocks at its top)
 
@@ -1456,21 +1476,33 @@ __global__ __launch_bounds__(256) void k_merge(MergeArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------
-hipError_t launch_partial(const PartialArgs& a, int grid, hipStream_t s) {
-  const bool paged = a.page_log2 > 0, big = a.T > 64;
+template <bool kPaged, bool kBigTree, bool kHelp, bool kRG>
+static void launch_partial_t(const PartialArgs& a, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((k_partial<kPaged, kBigTree, kHelp, kRG>), dim3(grid), dim3(kThreads), 0, s, a);
+}
+
+template <bool kPaged>
+static void launch_partial_p(const PartialArgs& a, int grid, hipStream_t s) {
+  const bool big = a.T > 64;
   const bool help = a.n_mtiles == 1 && a.M <= 2 * kRowsPerWave && !big;
-  if (help && paged)
-    hipLaunchKernelGGL((k_partial<true, false, true>), dim3(grid), dim3(kThreads), 0, s, a);
-  else if (help)
-    hipLaunchKernelGGL((k_partial<false, false, true>), dim3(grid), dim3(kThreads), 0, s, a);
-  else if (paged && big)
-    hipLaunchKernelGGL((k_partial<true, true, false>), dim3(grid), dim3(kThreads), 0, s, a);
-  else if (paged)
-    hipLaunchKernelGGL((k_partial<true, false, false>), dim3(grid), dim3(kThreads), 0, s, a);
+  const bool rg = a.n_mtiles == 1 && !help;
+  if (help)
+    launch_partial_t<kPaged, false, true, false>(a, grid, s);
+  else if (rg && big)
+    launch_partial_t<kPaged, true, false, true>(a, grid, s);
+  else if (rg)
+    launch_partial_t<kPaged, false, false, true>(a, grid, s);
   else if (big)
-    hipLaunchKernelGGL((k_partial<false, true, false>), dim3(grid), dim3(kThreads), 0, s, a);
+    launch_partial_t<kPaged, true, false, false>(a, grid, s);
   else
-    hipLaunchKernelGGL((k_partial<false, false, false>), dim3(grid), dim3(kThreads), 0, s, a);
+    launch_partial_t<kPaged, false, false, false>(a, grid, s);
+}
+
+hipError_t launch_partial(const PartialArgs& a, int grid, hipStream_t s) {
+  if (a.page_log2 > 0)
+    launch_partial_p<true>(a, grid, s);
+  else
+    launch_partial_p<false>(a, grid, s);
   return hipGetLastError();
 }
 

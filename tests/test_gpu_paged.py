@@ -25,6 +25,9 @@ PAGED = [
     (4, [2000, 33], 8, 8, 32768, 1024, 0),
     (5, [640], 33, 8, 4096, 32, 64),
     (6, [129], 3, 2, 4096, 8, 32),
+    # one M tile of 65..128 rows (gathers staged in VGPRs), also with a big tree
+    (7, [1500, 300], 16, 8, 16384, 16, 0),
+    (8, [700], 100, 1, 8192, 32, 0),
 ]
 
 

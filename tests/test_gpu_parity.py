@@ -78,6 +78,9 @@ SMALL = [
     # ragged prefixes that round up past one workgroup per CU: the split search
     (21, [30000] + [200] * 40, 2, 8, "random", 0),
     (22, [9000, 130, 4000, 131, 700, 129] * 4, 32, 16, "random", 0),
+    # one M tile of 65..128 rows (gathers staged in VGPRs): big tree, fixed split with a tail
+    (23, [900], 100, 1, "random", 0),
+    (24, [1234], 16, 8, "forest", 96),
 ]
 
 
