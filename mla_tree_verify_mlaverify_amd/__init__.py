@@ -18,6 +18,7 @@ from .binding import (  # noqa: F401
     Verifier,
     load_library,
     make_config,
+    probe_gather,
     run_static,
     status_string,
     tree_masks,

@@ -69,3 +69,16 @@ def test_more_than_one_gpu_is_refused():
                        text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_every_package_name_the_bench_calls_exists():
+    # the bench reaches the library only through the package: each `mv.<name>` it uses must be
+    # exported (a missing one would only show on the GPU, in the middle of the default run)
+    import re
+
+    import mla_tree_verify_mlaverify_amd as mv
+
+    names = set(re.findall(r"\bmv\.([A-Za-z_]\w*)", open(os.path.join(ROOT, "bench.py")).read()))
+    assert names and "probe_gather" in names
+    missing = sorted(n for n in names if not hasattr(mv, n))
+    assert not missing, missing
