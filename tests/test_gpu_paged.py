@@ -51,11 +51,11 @@ def test_paged_equals_its_expansion_and_oracle(seed, prefix, t, h, slots, page, 
     compare(a, la, ref_out, ref_lse)
 
 
-def test_paged_restart_on_the_helper_path():
+def test_paged_reference_raise_on_the_helper_path():
     # 64 rows in one M tile (the helper-wave path), fixed 256-token units, and in each request
     # a dominant key at prefix position 100: the fourth tile of the first unit raises every
-    # row's reference, so the unit starts over and gathers its first two tiles through the
-    # block table again
+    # row's reference, so each row's accumulator and sum are rescaled once mid-unit while the
+    # helper waves keep gathering through the block table
     cfg = synth.paged_config(9, batch=2, prefix=[1500, 700], tree_nodes=8, heads=8, slots=16384, page=16)
     flat = expanded(cfg)
     u = np.where(np.random.default_rng(9).integers(0, 2, size=synth.LATENT_DIM) == 1, 1.0, -1.0).astype(np.float32)

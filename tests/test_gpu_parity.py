@@ -171,7 +171,7 @@ def test_variant_parity(variant):
 @pytest.mark.parametrize("variant", ["sharp", "needle_prefix", "needle_tree", "prefix0", "chain", "qzero"])
 def test_variant_parity_one_m_tile(variant):
     # 64 rows in one M tile, three units; the needles raise a row's reference after its
-    # first tile (a restart of the unit)
+    # first tile (a rescale of the row's accumulator and sum)
     cfg = synth.make_config(0, variant=variant)
     out, lse, _ = run_gpu(cfg)
     ref_out, ref_lse = run_oracle(cfg)
