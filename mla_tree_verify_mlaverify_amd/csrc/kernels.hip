@@ -710,7 +710,7 @@ template <bool kPaged>
 // more rows; no other workgroup reads the same keys, so every gather goes to HBM, and the
 // compute waves stage their pieces in VGPRs (plain non-temporal 16-byte loads, which reach a
 // higher rate from HBM than direct-to-LDS loads) and write them to LDS at the end of the
-// iteration; the loop then has one body, which leaves the registers for the stage.
+// iteration.
 template <bool kPaged, bool kBigTree, bool kHelp, bool kRG>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_partial(PartialArgs a) {
@@ -1308,16 +1308,12 @@ void k_partial(PartialArgs a) {
     t++;
     return 0;
   };
-  if constexpr (kRG) {
-    for (int c = 0; c == 0;) c = iteration(IntC<0>{});
-  } else {
-    // The steady tiles run in a loop of their own: one body per loop, so that the values
-    // carried from one iteration to the next stay in place (a single loop dispatching to
-    // either body made the compiler copy them at every edge: 4% slower).
-    for (;;) {
-      while (t + 3 < nfull && !need_init) (void)iteration(IntC<1>{});
-      if (iteration(IntC<0>{})) break;
-    }
+  // The steady tiles run in a loop of their own: one body per loop, so that the values
+  // carried from one iteration to the next stay in place (a single loop dispatching to
+  // either body made the compiler copy them at every edge: 4% slower, and 24 more VGPRs).
+  for (;;) {
+    while (t + 3 < nfull && !need_init) (void)iteration(IntC<1>{});
+    if (iteration(IntC<0>{})) break;
   }
   // (the iteration that found the end ran the last tile's deferred PV blocks at its top)
 
