@@ -78,9 +78,10 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def stored_traffic(workload: str):
-    """HBM bytes per k_partial launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary of this
-    workload, or None when there is none or the kernel sources changed since the counters were taken."""
+def stored_profile(workload: str):
+    """The committed rocprofv3 summary of k_partial on this workload (HBM bytes per launch,
+    L2 hit rate, occupancy), or None when there is none or the kernel sources changed since
+    the counters were taken."""
     path = os.path.join(ROOT, "profiles", f"k_partial_{workload}.md")
     if not os.path.exists(path):
         return None
@@ -89,7 +90,23 @@ def stored_traffic(workload: str):
     if not m:
         return None
     tr = json.loads(m.group(1))
-    return tr["bytes_per_launch"] if tr.get("source_sha256_16") == source_hash() else None
+    return tr if tr.get("source_sha256_16") == source_hash() else None
+
+
+def stored_traffic(workload: str):
+    """HBM bytes per k_partial launch from the committed FETCH_SIZE/WRITE_SIZE counters of this
+    workload (see stored_profile), or None."""
+    tr = stored_profile(workload)
+    return tr["bytes_per_launch"] if tr else None
+
+
+def profile_fields(workload: str) -> dict:
+    """L2 hit rate and occupancy of k_partial on this workload from its committed summary
+    (null when absent or stale)."""
+    tr = stored_profile(workload) or {}
+    occ = {k: tr[k] for k in ("waves_per_simd", "workgroups_per_cu", "vgprs", "lds_bytes") if k in tr}
+    return {"l2_hit_rate": tr.get("l2_hit_rate"), "occupancy": occ or None,
+            "profile": f"profiles/k_partial_{workload}.md" if tr else None}
 
 
 def lscpu_model() -> str:
@@ -467,6 +484,8 @@ def main() -> int:
     line.update({k: summ[k] for k in ("us_per_call", "kernels_us", "pct_hbm_peak", "pct_hbm_measured", "tflops",
                                       "pct_mfma_peak", "roofline_frac_call", "sclk_mhz", "plan")})
     line["roofline"] = roof
+    if not (args.variant or args.split or args.warm or args.page > 1):
+        line.update(profile_fields(synth.CONFIGS[args.config]["name"]))
     del res
     if not args.no_per_config and args.config == 3 and not (args.variant or args.page > 1 or args.split):
         # the other seeded workloads, timed in the same run with the same protocol (fewer calls)
@@ -477,6 +496,8 @@ def main() -> int:
             r = time_verify(c, args, flush, steps, min(args.warmup, 3), graph=False, split=0, page=0)
             per[name] = verify_summary(c, algorithmic_counts(c), r, copy_gbs)
             per[name]["steps"] = steps
+            if var is None:
+                per[name].update(profile_fields(name))
             del r, c
             torch.cuda.empty_cache()
         line["per_config"] = per

@@ -62,6 +62,12 @@ def test_stored_traffic_follows_the_kernel_sources():
     else:
         assert got is None
     assert bench.stored_traffic("no_such_workload") is None
+    f = bench.profile_fields("p185000_t64_h8")
+    if recorded == bench.source_hash():
+        assert 0.0 < f["l2_hit_rate"] < 1.0 and f["occupancy"]["waves_per_simd"] >= 1
+    else:
+        assert f["l2_hit_rate"] is None and f["occupancy"] is None
+    assert bench.profile_fields("no_such_workload") == {"l2_hit_rate": None, "occupancy": None, "profile": None}
 
 
 def test_more_than_one_gpu_is_refused():
