@@ -511,8 +511,10 @@ def main() -> int:
 
 # The seeded workloads other than the 185k headline, each timed once per default run: the
 # 4k and 65k prefixes (the 65k one also with its indices sorted, and as one contiguous run),
-# the batch of 8, and the two HBM-bound small-tree shapes.
-PER_CONFIG = [(1, None), (2, None), (2, "sorted"), (2, "contiguous"), (4, None), (5, None), (6, None)]
+# the batch of 8, and the two HBM-bound small-tree shapes (each also as one contiguous run,
+# where the fast path's savings would show first).
+PER_CONFIG = [(1, None), (2, None), (2, "sorted"), (2, "contiguous"), (4, None), (5, None), (5, "contiguous"),
+              (6, None), (6, "contiguous")]
 
 
 def verify_workload(i: int, variant, page: int):

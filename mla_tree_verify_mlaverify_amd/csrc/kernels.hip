@@ -510,13 +510,20 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
 // uniformly over the workgroup, when the batch needs plan_units instead: more than 64
 // requests, or ragged requests whose unit count rounds past the target (the split search).
 // Fills up for unit g; a publishing wave writes the plan out.
-__device__ bool plan_wave(const PartialArgs& a, int g, bool publish, UnitPlan& up) {
+template <class Hook>
+__device__ bool plan_wave(const PartialArgs& a, int g, bool publish, UnitPlan& up, Hook&& after_loads) {
   const int B = a.batch, T = a.T;
-  if (B > 64) return false;
+  if (B > 64) {
+    after_loads();
+    return false;
+  }
   const int lane = threadIdx.x & 63;
   const bool in = lane < B;
   int pv = a.prefix_lens[min(lane, B - 1)];
   int tl = a.tree_lens ? a.tree_lens[min(lane, B - 1)] : T;
+  __builtin_amdgcn_sched_barrier(0);
+  after_loads();
+  __builtin_amdgcn_sched_barrier(0);
   const int bp = (in && (pv < 0 || pv > a.max_prefix)) ? 1 : 0;
   const int bt = (in && (tl < 1 || tl > T)) ? 1 : 0;
   const int run_bad = wave_incl_scan(bp + (bt << 16));  // bad prefix lengths low, tree lengths high
@@ -746,9 +753,29 @@ void k_partial(PartialArgs a) {
     clk0 = __builtin_amdgcn_s_memtime();
     rt0 = __builtin_amdgcn_s_memrealtime();
   }
+  // Every workgroup of the launch reads the Q rows of its M tile, all at once, when its plan
+  // is known.  So that those reads find Q in L2 rather than all miss together, the
+  // workgroups of each XCD (consecutive ids go to consecutive XCDs) first touch one slice
+  // each of the call's Q, one 4-byte load per 128-byte line, while the plan's own loads are
+  // in flight.  Ragged calls (Q size known only from the plan) and large Q skip it.
+  uint32_t qpf0 = 0, qpf1 = 0;
+  auto prefetch_q = [&]() {
+    const int64_t qbytes = a.tree_lens ? 0 : (int64_t)a.batch * a.M * kRowBytes;
+    const int xwg = ((int)gridDim.x - (bid & 7) + 7) >> 3;  // workgroups on this XCD
+    const int64_t nl = (qbytes + 127) >> 7;
+    const int64_t l0 = nl * (bid >> 3) / xwg, l1 = nl * ((bid >> 3) + 1) / xwg;
+    if (qbytes > 0 && l1 - l0 <= 2 * kThreads) {
+      const char* qc = reinterpret_cast<const char*>(a.q);
+      const int64_t la = l0 + tid, lb = l0 + kThreads + tid;
+      if (la < l1) qpf0 = *reinterpret_cast<const uint32_t*>(qc + min(la << 7, qbytes - 4));
+      if (lb < l1) qpf1 = *reinterpret_cast<const uint32_t*>(qc + min(lb << 7, qbytes - 4));
+    }
+  };
   // (tile buffer 0 is the plan's scratch: no gather writes it before the plan is done)
   UnitPlan up;
-  if (!plan_wave(a, g, g == 0 && mt == 0 && wu == 0, up)) {
+  const bool planned = plan_wave(a, g, g == 0 && mt == 0 && wu == 0, up, prefetch_q);
+  asm volatile("" ::"v"(qpf0), "v"(qpf1));  // the touches have landed (none in flight at any return)
+  if (!planned) {
     up.total = plan_units(a, g, g == 0 && mt == 0, s_tmp, s_unit, reinterpret_cast<int*>(smem));
     up.b = s_unit[0];
     up.key_off = s_unit[1];
