@@ -598,19 +598,19 @@ __device__ bool plan_wave(const PartialArgs& a, int g, bool publish, UnitPlan& u
 // inlined behind a marker that the build's register audit knows (these waves may use the
 // AGPRs, the compute waves may not); it never returns, the waves end in it.  pidx / tidx are
 // the prefix and tree parts of the unit's index segment, as in the kernel.
-template <bool kPaged>
+template <bool kPaged, class Checks>
 [[noreturn]] __device__ __attribute__((always_inline)) inline void gather_helper(const char* pool_in, int64_t row_stride_bytes,
                                                         int64_t pool_slots, int T, int page_log2, int max_page,
                                                         const int32_t* pidx, const int32_t* tidx, int kbeg, int npk,
-                                                        int npt, int ntiles, int run_base, int bad_index,
-                                                        char* smem) {
+                                                        int npt, int ntiles, int run_base, char* smem,
+                                                        Checks&& checks) {
   typedef __attribute__((address_space(1))) const char gmem_char;
   gmem_char* pool = (gmem_char*)pool_in;
   typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
   lds_char* lds = (lds_char*)smem;
   const int tid = threadIdx.x;
   const int hh = tid - 2 * 64, hk = hh >> 3, hc = hh & 7;
-  int bad = bad_index;
+  int bad = 0;
   const int pmask = (1 << page_log2) - 1;
   auto page_slot = [&](int e, int pos) -> int {
     return (uint32_t)e <= (uint32_t)max_page ? (e << page_log2) + (pos & pmask) : -1;
@@ -635,14 +635,6 @@ template <bool kPaged>
     const bool oob = (uint32_t)idx >= (uint64_t)pool_slots;
     bad |= oob ? 1 : 0;
     return (const char*)(pool + (uint64_t)(oob ? 0u : (uint32_t)idx) * (uint64_t)row_stride_bytes);
-  };
-  auto tile0_barrier = [&]() {  // start_scores: tile 0 has landed everywhere
-    if (ntiles > 1) {
-      __builtin_amdgcn_s_waitcnt(0x0F79);  // vmcnt(9)
-    } else {
-      __builtin_amdgcn_s_waitcnt(0x0F70);
-    }
-    __syncthreads();
   };
   auto entries = [&](int (&en)[2], int tl) {
 #pragma unroll
@@ -669,18 +661,32 @@ template <bool kPaged>
   };
   u32x4 st0[18], st1[18];
   int en0[2], en1[2];  // index entries of the tile each stage loads next
-  // Stage 0 gets tile 2 and stage 1 tile 3, en0 and en1 the entries of tiles 4 and 5, in an
-  // order (rows, then the entries they lead to) that lets each wait below leave the other
-  // stage in flight, since loads complete in issue order.
-  auto start = [&]() {
-    int e2[2], e3[2];
-    entries(e2, 2);
-    entries(e3, 3);
-    rows(st0, 2, e2);
-    entries(en0, 4);
-    rows(st1, 3, e3);
-    entries(en1, 5);
-  };
+  // Tiles 0 and 1 go out first, one per stage, each followed by the entries of the tile its
+  // stage loads next (2 and 3), an order that lets each wait below leave the other stage in
+  // flight, since loads complete in issue order.
+  {
+    int e0[2], e1[2];
+    entries(e0, 0);
+    entries(e1, 1);
+    rows(st0, 0, e0);
+    entries(en0, 2);
+    rows(st1, 1, e1);
+    entries(en1, 3);
+  }
+  if (checks()) {  // the tree check found a bad parent: the workgroup ends
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __builtin_amdgcn_endpgm();
+  }
+  // Tile 0 into its buffer before the compute waves' first scores, tile 1 after them (its
+  // buffer is not read before the next barrier); the stages then hold tiles 2 and 3 and en0
+  // and en1 the entries of tiles 4 and 5, as the loop expects.
+  write(st0, 0);
+  rows(st0, 2, en0);
+  entries(en0, 4);
+  __syncthreads();
+  if (ntiles > 1) write(st1, 1);
+  rows(st1, 3, en1);
+  entries(en1, 5);
   // Iteration t: tile t+2 (in the stage of t's parity) goes to its buffer, which held tile
   // t-1 and is free after this iteration's barrier; the stage then loads tile t+4.
   auto step = [&](u32x4 (&st)[18], int (&en)[2], int tl) {
@@ -692,8 +698,6 @@ template <bool kPaged>
   // the last.  It is unrolled by two, one stage per half, so that every path into its head
   // leaves the loads in the same order (st0, en0, st1, en1) and the compiler's waits stay
   // counted.
-  tile0_barrier();
-  start();
   for (int t = 0;;) {
     __syncthreads();
     if (t == ntiles) break;
@@ -900,7 +904,7 @@ void k_partial(PartialArgs a) {
     if (tid < npk) run_mine = slot_at(tid);
   }
   int raw0 = 0, raw1 = 0, raw2 = 0;  // index-table entries of tiles 0..2 (this thread's key)
-  if (plan_ok) {
+  if (plan_ok && !kHelp) {
     raw0 = load_index(0);
     if (ntiles > 1) raw1 = load_index(1);
     if (ntiles > 2) raw2 = load_index(2);
@@ -912,7 +916,7 @@ void k_partial(PartialArgs a) {
   // the rest (loaded first) are parked in this wave's LDS slice once they land.  Rows past
   // M (last M tile) read the request's last row; their results are dropped.
   u32x4 qf[kQReg], qt[36 - kQReg];
-  if (plan_ok) {
+  if (plan_ok && (!kHelp || wu < 2)) {
     const u32x4* qp =
         reinterpret_cast<const u32x4*>(a.q + ((size_t)node_off * a.H + (rvalid ? r : Mb - 1)) * kLatent) + h;
 #pragma unroll
@@ -1202,16 +1206,34 @@ void k_partial(PartialArgs a) {
   };
   // Then, once tile 0 has landed everywhere, its scores.
   auto start_scores = [&]() {
-    if (ntiles > 1) {
-      __builtin_amdgcn_s_waitcnt(0x0F79);  // vmcnt(9): tile 0 landed (tile 1 may not)
-    } else {
-      __builtin_amdgcn_s_waitcnt(0x0F70);
+    if constexpr (!kHelp) {
+      if (ntiles > 1) {
+        __builtin_amdgcn_s_waitcnt(0x0F79);  // vmcnt(9): tile 0 landed (tile 1 may not)
+      } else {
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+      }
     }
     __syncthreads();
     need_init = __any(mref == -INFINITY);
     sacc = s_chain(IntC<-1>{}, IntC<0>{}, lds, nullptr, 0u, zero16, 0.f, dummy_soft, s_pre(lds));
   };
-  start_gathers(raw0, raw1, raw2);
+  if constexpr (kHelp) {
+    if (wu >= 2) {
+      // From here on only the helper waves run; they hold no rows, so the build's register
+      // audit lets the compiler use AGPRs past this marker.  They gather every tile of the
+      // unit, tiles 0 and 1 included, and take part in the tree check.
+      asm volatile("; mlv-helper-waves" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);  // keep the helper's code below the marker
+      gather_helper<kPaged>(reinterpret_cast<const char*>(a.pool), a.row_stride_bytes, a.pool_slots, Tb,
+                            a.page_log2, a.max_page, pidx, tidx, kbeg, npk, npt, ntiles, run_base, smem,
+                            [&]() -> bool {
+                              if (last) masks();
+                              return req_err != 0;
+                            });
+    }
+  } else {
+    start_gathers(raw0, raw1, raw2);
+  }
   MLV_ZERO_O();  // O^T[d = 32db + ..][row] accumulates in a[0..255]
   if (last) masks();
   if (req_err) {  // a bad parent: the tiles' gathers must land before the workgroup ends
@@ -1223,17 +1245,6 @@ void k_partial(PartialArgs a) {
   for (int kk = kQReg; kk < 36; kk++) qlds[(kk - kQReg) * 64] = qt[kk - kQReg];  // lane-major, conflict-free
 #pragma unroll
   for (int w = 0; w < kW; w++) anc[w] = (last && rvalid) ? s_m[(r / a.H) * kW + w] : ~0ull;
-  if constexpr (kHelp) {
-    if (wu >= 2) {
-      // From here on only the helper waves run; they hold no rows, so the build's register
-      // audit lets the compiler use AGPRs past this marker.
-      asm volatile("; mlv-helper-waves" ::: "memory");
-      __builtin_amdgcn_sched_barrier(0);  // keep the helper's code below the marker
-      gather_helper<kPaged>(reinterpret_cast<const char*>(a.pool), a.row_stride_bytes, a.pool_slots, Tb,
-                            a.page_log2, a.max_page, pidx, tidx, kbeg, npk, npt, ntiles, run_base, bad_index, smem);
-      return;
-    }
-  }
   start_scores();
   // Deferred PV fragments and their P operand; zero before the first tile, so that the
   // deferred MFMAs at the first barrier add nothing.
