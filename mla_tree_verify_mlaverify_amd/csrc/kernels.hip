@@ -1037,6 +1037,9 @@ void k_partial(PartialArgs a) {
   // them (s_pre) as early as the tile is known to be in LDS.
   constexpr int kSDist = 2;
   u32x4 rg[kRG ? 9 : 1];  // kRG: this thread's 9 pieces of tile t+2 on their way to LDS
+  // kRGStart: tiles 0 and 1 staged the same way (big trees' masks leave too few registers)
+  constexpr bool kRGStart = kRG && !kBigTree;
+  u32x4 rg1[kRGStart ? 9 : 1];  // tile 1's pieces, at the start
   struct SPre {
     u32x4 k[kSDist], q[kSDist];
   };
@@ -1206,7 +1209,12 @@ void k_partial(PartialArgs a) {
   };
   // Then, once tile 0 has landed everywhere, its scores.
   auto start_scores = [&]() {
-    if constexpr (!kHelp) {
+    if constexpr (kRGStart) {  // tile 0 from VGPRs into buffer 0
+      lds_u32x4* d = reinterpret_cast<lds_u32x4*>(lds) + tid;
+#pragma unroll
+      for (int j = 0; j < 9; j++) d[j * 256] = rg[j];
+    }
+    if constexpr (!kHelp && !kRGStart) {
       if (ntiles > 1) {
         __builtin_amdgcn_s_waitcnt(0x0F79);  // vmcnt(9): tile 0 landed (tile 1 may not)
       } else {
@@ -1231,6 +1239,16 @@ void k_partial(PartialArgs a) {
                               return req_err != 0;
                             });
     }
+  } else if constexpr (kRGStart) {
+    // tiles 0 and 1 through VGPRs as well: tile 0 goes to LDS before the first scores,
+    // tile 1 while they run
+    const char* src0 = tile_src(slot_of(0, raw0));
+    const char* src1 = tile_src(ntiles > 1 ? slot_of(1, raw1) : 0);
+    idx_next = raw2;
+#pragma unroll
+    for (int j = 0; j < 9; j++) rg[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src0 + 128 * j));
+#pragma unroll
+    for (int j = 0; j < 9; j++) rg1[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src1 + 128 * j));
   } else {
     start_gathers(raw0, raw1, raw2);
   }
@@ -1246,6 +1264,13 @@ void k_partial(PartialArgs a) {
 #pragma unroll
   for (int w = 0; w < kW; w++) anc[w] = (last && rvalid) ? s_m[(r / a.H) * kW + w] : ~0ull;
   start_scores();
+  if constexpr (kRGStart) {  // tile 1 into buffer 1 (read after the next barrier)
+    if (ntiles > 1) {
+      lds_u32x4* d = reinterpret_cast<lds_u32x4*>(lds + kTileBytes) + tid;
+#pragma unroll
+      for (int j = 0; j < 9; j++) d[j * 256] = rg1[j];
+    }
+  }
   // Deferred PV fragments and their P operand; zero before the first tile, so that the
   // deferred MFMAs at the first barrier add nothing.
   u32x4 vdef[kDeferArr][2], pdef[2];
