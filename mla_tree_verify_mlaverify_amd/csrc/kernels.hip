@@ -603,7 +603,7 @@ template <bool kPaged, class Checks>
                                                         int64_t pool_slots, int T, int page_log2, int max_page,
                                                         const int32_t* pidx, const int32_t* tidx, int kbeg, int npk,
                                                         int npt, int ntiles, int run_base, char* smem,
-                                                        Checks&& checks) {
+                                                        int e00, int e01, int e10, int e11, Checks&& checks) {
   typedef __attribute__((address_space(1))) const char gmem_char;
   gmem_char* pool = (gmem_char*)pool_in;
   typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
@@ -661,13 +661,12 @@ template <bool kPaged, class Checks>
   };
   u32x4 st0[18], st1[18];
   int en0[2], en1[2];  // index entries of the tile each stage loads next
-  // Tiles 0 and 1 go out first, one per stage, each followed by the entries of the tile its
-  // stage loads next (2 and 3), an order that lets each wait below leave the other stage in
+  // Tiles 0 and 1 go out first, one per stage (their entries e00 .. e11, keys hk and hk + 16,
+  // came with the kernel's first loads), each followed by the entries of the tile its stage
+  // loads next (2 and 3), an order that lets each wait below leave the other stage in
   // flight, since loads complete in issue order.
   {
-    int e0[2], e1[2];
-    entries(e0, 0);
-    entries(e1, 1);
+    const int e0[2] = {e00, e01}, e1[2] = {e10, e11};
     rows(st0, 0, e0);
     entries(en0, 2);
     rows(st1, 1, e1);
@@ -835,15 +834,17 @@ void k_partial(PartialArgs a) {
   // Pool slot of this thread's key of tile t (tail keys re-read the tile's first key), in two
   // steps: load_index issues the table load, slot_of turns its value into the slot once it is
   // needed (a contiguous prefix run ignores the value), so no wait follows the load.
-  auto key_of = [&](int t) -> int {
+  auto key_at = [&](int t, int k) -> int {
     const int nv = t < npt ? min(kTileKeys, npk - t * kTileKeys) : min(kTileKeys, Tb - (t - npt) * kTileKeys);
-    return kt < nv ? kt : 0;
+    return k < nv ? k : 0;
   };
-  auto load_index = [&](int t) -> int {
-    if (kPaged && t < npt) return pidx[(kbeg + t * kTileKeys + key_of(t)) >> a.page_log2];
+  auto key_of = [&](int t) -> int { return key_at(t, kt); };
+  auto load_index_at = [&](int t, int k) -> int {
+    if (kPaged && t < npt) return pidx[(kbeg + t * kTileKeys + key_at(t, k)) >> a.page_log2];
     const int32_t* ip = t < npt ? pidx + t * kTileKeys : tidx + (t - npt) * kTileKeys;
-    return ip[key_of(t)];
+    return ip[key_at(t, k)];
   };
+  auto load_index = [&](int t) -> int { return load_index_at(t, kt); };
   auto slot_of = [&](int t, int loaded) -> int {
     if (t < npt && run_base >= 0) return run_base + t * kTileKeys + key_of(t);
     if (kPaged && t < npt) return page_slot(loaded, kbeg + t * kTileKeys + key_of(t));
@@ -903,11 +904,24 @@ void k_partial(PartialArgs a) {
     run_first = slot_at(0);
     if (tid < npk) run_mine = slot_at(tid);
   }
-  int raw0 = 0, raw1 = 0, raw2 = 0;  // index-table entries of tiles 0..2 (this thread's key)
-  if (plan_ok && !kHelp) {
-    raw0 = load_index(0);
-    if (ntiles > 1) raw1 = load_index(1);
-    if (ntiles > 2) raw2 = load_index(2);
+  // Index-table entries of tiles 0..2 (this thread's key); in the helper waves those of
+  // tiles 0 and 1 for their two keys, kt - 16 and kt.
+  int raw0 = 0, raw1 = 0, raw2 = 0, raw3 = 0;
+  if (plan_ok) {
+    if constexpr (kHelp) {
+      if (wu >= 2) {
+        raw0 = load_index_at(0, kt - 16);
+        raw1 = load_index_at(0, kt);
+        if (ntiles > 1) {
+          raw2 = load_index_at(1, kt - 16);
+          raw3 = load_index_at(1, kt);
+        }
+      }
+    } else {
+      raw0 = load_index(0);
+      if (ntiles > 1) raw1 = load_index(1);
+      if (ntiles > 2) raw2 = load_index(2);
+    }
   }
   int par_i = 0;
   if (last && tid < Tb) par_i = a.tree_parent[(size_t)node_off + tid];
@@ -1234,7 +1248,7 @@ void k_partial(PartialArgs a) {
       __builtin_amdgcn_sched_barrier(0);  // keep the helper's code below the marker
       gather_helper<kPaged>(reinterpret_cast<const char*>(a.pool), a.row_stride_bytes, a.pool_slots, Tb,
                             a.page_log2, a.max_page, pidx, tidx, kbeg, npk, npt, ntiles, run_base, smem,
-                            [&]() -> bool {
+                            raw0, raw1, raw2, raw3, [&]() -> bool {
                               if (last) masks();
                               return req_err != 0;
                             });
