@@ -295,8 +295,9 @@ MLAVERIFY_API int mlaverify_read_device_errors(mlaverify_t h, void* stream, uint
 /* Kernel timing for benchmarks (not for graph capture).  The "Chunk 66.0" summary finds
  * that the reduction kernel and the tile sizing still needed work; these events time the
  * partial pass and the merge apart, on the run's own stream.  After
- * mlaverify_profile_begin(h, n) the next n calls of mlaverify_run (or _ragged) record HIP events
- * on their stream before and after each of their two kernels (partial pass, merge).
+ * mlaverify_profile_begin(h, n) the next n calls of mlaverify_run (or _ragged) launch their two
+ * kernels (partial pass, merge) with a pair of HIP events each that take the begin and end
+ * timestamps of the kernel's own dispatch on the run's stream.
  * mlaverify_profile_end synchronises on the last event, writes host_ms[2*i + k] =
  * duration in milliseconds of kernel k of recorded run i for
  * i < min(runs, capacity_runs), releases the events and returns the number of runs

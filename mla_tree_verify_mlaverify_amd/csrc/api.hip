@@ -82,7 +82,7 @@ struct mlaverify_handle {
   bool owns_ws;
   Layout L;
   int last_batch;
-  std::vector<hipEvent_t> prof_events;  // 3 per profiled run
+  std::vector<hipEvent_t> prof_events;  // 4 per profiled run
   int prof_max = 0, prof_runs = 0;
 };
 
@@ -134,7 +134,8 @@ size_t run_offsets(const mlaverify_config& c, int batch, int T, RunOffsets* o) {
 }
 
 // Enqueues the two kernels of one verify pass (plan + partials, then the merge) over the
-// workspace areas w; records the profiling events ev[0..2] around them when ev is given.
+// workspace areas w; when ev is given, ev[0..1] and ev[2..3] take the begin and end
+// timestamps of the two kernels' dispatches.
 int enqueue_run(const mlaverify_config& c, const RunAreas& w, int batch, int T, const int32_t* tree_lens,
                 const void* q, const void* kv_pool, const int32_t* kv_indices, const int32_t* prefix_lens,
                 const int32_t* tree_parent, void* out, float* lse, hipStream_t s, hipEvent_t* ev) {
@@ -189,11 +190,8 @@ int enqueue_run(const mlaverify_config& c, const RunAreas& w, int batch, int T, 
                                      : (int)cdiv(ka.target_units, batch);
 
   const int grid = n_mt * (int)(cdiv(units_grid, 8) * 8);
-  if (ev && hipEventRecord(ev[0], s) != hipSuccess) return MLAVERIFY_ERR_HIP;
-  if (launch_partial(ka, grid, s) != hipSuccess) return MLAVERIFY_ERR_HIP;
-  if (ev && hipEventRecord(ev[1], s) != hipSuccess) return MLAVERIFY_ERR_HIP;
-  if (launch_merge(ma, s) != hipSuccess) return MLAVERIFY_ERR_HIP;
-  if (ev && hipEventRecord(ev[2], s) != hipSuccess) return MLAVERIFY_ERR_HIP;
+  if (launch_partial(ka, grid, s, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr) != hipSuccess) return MLAVERIFY_ERR_HIP;
+  if (launch_merge(ma, s, ev ? ev[2] : nullptr, ev ? ev[3] : nullptr) != hipSuccess) return MLAVERIFY_ERR_HIP;
   return MLAVERIFY_OK;
 }
 
@@ -315,7 +313,7 @@ int mlaverify_run(mlaverify_t hd, int32_t batch, int32_t T, const void* q, const
                       reinterpret_cast<int32_t*>(hd->ws + L.unit_tab), reinterpret_cast<float*>(hd->ws + L.part_lse),
                       reinterpret_cast<uint16_t*>(hd->ws + L.part_o)};
   hipEvent_t* ev = nullptr;
-  if (hd->prof_runs < hd->prof_max) ev = &hd->prof_events[3 * hd->prof_runs++];
+  if (hd->prof_runs < hd->prof_max) ev = &hd->prof_events[4 * hd->prof_runs++];
   const int rc = enqueue_run(c, w, batch, T, nullptr, q, kv_pool, kv_indices, prefix_lens, tree_parent, out, lse,
                              static_cast<hipStream_t>(stream), ev);
   if (rc == MLAVERIFY_OK) hd->last_batch = batch;
@@ -336,7 +334,7 @@ int mlaverify_run_ragged(mlaverify_t hd, int32_t batch, int32_t max_T, const int
                       reinterpret_cast<int32_t*>(hd->ws + L.unit_tab), reinterpret_cast<float*>(hd->ws + L.part_lse),
                       reinterpret_cast<uint16_t*>(hd->ws + L.part_o)};
   hipEvent_t* ev = nullptr;
-  if (hd->prof_runs < hd->prof_max) ev = &hd->prof_events[3 * hd->prof_runs++];
+  if (hd->prof_runs < hd->prof_max) ev = &hd->prof_events[4 * hd->prof_runs++];
   const int rc = enqueue_run(c, w, batch, max_T, tree_lens, q, kv_pool, kv_indices, prefix_lens, tree_parent, out,
                              lse, static_cast<hipStream_t>(stream), ev);
   if (rc == MLAVERIFY_OK) hd->last_batch = batch;
@@ -507,7 +505,7 @@ int mlaverify_read_device_errors(mlaverify_t hd, void* stream, uint32_t* flags) 
 int mlaverify_profile_begin(mlaverify_t hd, int32_t max_runs) {
   if (!hd || max_runs < 1 || max_runs > (1 << 20)) return MLAVERIFY_ERR_INVALID_ARG;
   release_profile(hd);
-  hd->prof_events.resize(3 * (size_t)max_runs);
+  hd->prof_events.resize(4 * (size_t)max_runs);
   for (size_t i = 0; i < hd->prof_events.size(); i++) {
     if (hipEventCreate(&hd->prof_events[i]) != hipSuccess) {
       hd->prof_events.resize(i);
@@ -524,10 +522,10 @@ int mlaverify_profile_end(mlaverify_t hd, float* host_ms, int32_t capacity_runs)
   if (!hd || capacity_runs < 0 || (capacity_runs > 0 && !host_ms)) return MLAVERIFY_ERR_INVALID_ARG;
   const int runs = hd->prof_runs;
   int rc = runs;
-  if (runs > 0 && hipEventSynchronize(hd->prof_events[3 * runs - 1]) != hipSuccess) rc = MLAVERIFY_ERR_HIP;
+  if (runs > 0 && hipEventSynchronize(hd->prof_events[4 * runs - 1]) != hipSuccess) rc = MLAVERIFY_ERR_HIP;
   for (int i = 0; rc >= 0 && i < runs && i < capacity_runs; i++)
     for (int k = 0; k < 2; k++)
-      if (hipEventElapsedTime(&host_ms[2 * i + k], hd->prof_events[3 * i + k], hd->prof_events[3 * i + k + 1]) !=
+      if (hipEventElapsedTime(&host_ms[2 * i + k], hd->prof_events[4 * i + 2 * k], hd->prof_events[4 * i + 2 * k + 1]) !=
           hipSuccess)
         rc = MLAVERIFY_ERR_HIP;
   release_profile(hd);

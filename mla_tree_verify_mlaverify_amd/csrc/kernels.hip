@@ -1550,59 +1550,69 @@ __global__ __launch_bounds__(256) void k_merge(MergeArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------
+// A launch; with events, hipExtLaunchKernelGGL has them take the dispatch's own timestamps.
+template <class K, class A>
+static void launch_timed(K kernel, int grid, int block, hipStream_t s, hipEvent_t start, hipEvent_t stop,
+                         const A& args) {
+  if (start || stop)
+    hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(block), 0, s, start, stop, 0, args);
+  else
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(block), 0, s, args);
+}
+
 template <bool kPaged, bool kBigTree, bool kHelp, bool kRG>
-static void launch_partial_t(const PartialArgs& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((k_partial<kPaged, kBigTree, kHelp, kRG>), dim3(grid), dim3(kThreads), 0, s, a);
+static void launch_partial_t(const PartialArgs& a, int grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  launch_timed(k_partial<kPaged, kBigTree, kHelp, kRG>, grid, kThreads, s, e0, e1, a);
 }
 
 template <bool kPaged>
-static void launch_partial_p(const PartialArgs& a, int grid, hipStream_t s) {
+static void launch_partial_p(const PartialArgs& a, int grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   const bool big = a.T > 64;
   const bool help = a.n_mtiles == 1 && a.M <= 2 * kRowsPerWave && !big;
   const bool rg = a.n_mtiles == 1 && !help;
   if (help)
-    launch_partial_t<kPaged, false, true, false>(a, grid, s);
+    launch_partial_t<kPaged, false, true, false>(a, grid, s, e0, e1);
   else if (rg && big)
-    launch_partial_t<kPaged, true, false, true>(a, grid, s);
+    launch_partial_t<kPaged, true, false, true>(a, grid, s, e0, e1);
   else if (rg)
-    launch_partial_t<kPaged, false, false, true>(a, grid, s);
+    launch_partial_t<kPaged, false, false, true>(a, grid, s, e0, e1);
   else if (big)
-    launch_partial_t<kPaged, true, false, false>(a, grid, s);
+    launch_partial_t<kPaged, true, false, false>(a, grid, s, e0, e1);
   else
-    launch_partial_t<kPaged, false, false, false>(a, grid, s);
+    launch_partial_t<kPaged, false, false, false>(a, grid, s, e0, e1);
 }
 
-hipError_t launch_partial(const PartialArgs& a, int grid, hipStream_t s) {
+hipError_t launch_partial(const PartialArgs& a, int grid, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
   if (a.page_log2 > 0)
-    launch_partial_p<true>(a, grid, s);
+    launch_partial_p<true>(a, grid, s, start, stop);
   else
-    launch_partial_p<false>(a, grid, s);
+    launch_partial_p<false>(a, grid, s, start, stop);
   return hipGetLastError();
 }
 
 template <int kSplit>
-static void launch_merge_split(const MergeArgs& a, int rows, hipStream_t s) {
+static void launch_merge_split(const MergeArgs& a, int rows, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   // kDepth: the smallest of 2, 4, 8 units per slot that holds the launch's units in one round
   constexpr int kSlots = kWaves * 64 / (kVdim / kSplit / 8);
   const int depth = a.units_hint <= 2 * kSlots ? 2 : a.units_hint <= 4 * kSlots ? 4 : 8;
   if (depth == 2)
-    hipLaunchKernelGGL((k_merge<kSplit, 8, 2>), dim3(rows * kSplit), dim3(256), 0, s, a);
+    launch_timed(k_merge<kSplit, 8, 2>, rows * kSplit, 256, s, e0, e1, a);
   else if (depth == 4)
-    hipLaunchKernelGGL((k_merge<kSplit, 8, 4>), dim3(rows * kSplit), dim3(256), 0, s, a);
+    launch_timed(k_merge<kSplit, 8, 4>, rows * kSplit, 256, s, e0, e1, a);
   else
-    hipLaunchKernelGGL((k_merge<kSplit, 8, 8>), dim3(rows * kSplit), dim3(256), 0, s, a);
+    launch_timed(k_merge<kSplit, 8, 8>, rows * kSplit, 256, s, e0, e1, a);
 }
 
-hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
+hipError_t launch_merge(const MergeArgs& a, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
   // about kMergeBlocks workgroups: up to 8 per row when rows are few, whole rows when many;
   // 16-byte lanes throughout
   const int rows = a.batch * a.M;
   const int split = rows * 8 <= kMergeBlocks ? 8 : rows * 4 <= kMergeBlocks ? 4 : rows * 2 <= kMergeBlocks ? 2 : 1;
   switch (split) {
-    case 8: launch_merge_split<8>(a, rows, s); break;
-    case 4: launch_merge_split<4>(a, rows, s); break;
-    case 2: launch_merge_split<2>(a, rows, s); break;
-    default: launch_merge_split<1>(a, rows, s); break;
+    case 8: launch_merge_split<8>(a, rows, s, start, stop); break;
+    case 4: launch_merge_split<4>(a, rows, s, start, stop); break;
+    case 2: launch_merge_split<2>(a, rows, s, start, stop); break;
+    default: launch_merge_split<1>(a, rows, s, start, stop); break;
   }
   return hipGetLastError();
 }

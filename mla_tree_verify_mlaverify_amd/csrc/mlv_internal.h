@@ -1,6 +1,7 @@
 // Internal layout shared by the host library and the gfx950 kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -132,8 +133,11 @@ struct AcceptArgs {
 hipError_t launch_relocate(const RelocArgs& a, hipStream_t s);
 hipError_t launch_accept(const AcceptArgs& a, hipStream_t s);
 int accept_chunks(int64_t vocab);
-hipError_t launch_partial(const PartialArgs& a, int grid, hipStream_t s);
-hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
+// With start/stop events (profiling), the kernel is launched so that the events take the
+// begin and end timestamps of its own dispatch, not of separate markers around it.
+hipError_t launch_partial(const PartialArgs& a, int grid, hipStream_t s, hipEvent_t start = nullptr,
+                          hipEvent_t stop = nullptr);
+hipError_t launch_merge(const MergeArgs& a, hipStream_t s, hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 hipError_t launch_probe_gather(const void* pool, int64_t stride_bytes, int64_t slots, const int32_t* idx, int n,
                                int lds, int grid, uint32_t* sink, hipStream_t s);
 hipError_t launch_tree_masks(const int32_t* tree_parent, int batch, int T, uint64_t* masks, uint32_t* err,
