@@ -588,16 +588,18 @@ __device__ bool plan_wave(const PartialArgs& a, int g, bool publish, UnitPlan& u
 }
 
 // Gathers of a unit with at most 64 rows in one M tile, run by waves 2 and 3, which hold
-// no rows, so that the compute waves issue none after tiles 0 and 1.  Rows pass through
-// these waves' VGPRs (plain non-temporal 16-byte loads, which reach a higher rate from HBM
-// than LDS-DMA gathers) on their way to LDS.  Helper thread hh covers keys hk and hk + 16 of
-// a tile and chunk slot hc of each of the 9 groups.  Two register stages hold tiles t+2 and
-// t+3: each tile's loads go out two iterations before it is written to LDS, so that two
-// tiles are in flight.  The loop mirrors the compute waves' barriers one for one from their
-// first scores on: that barrier, one per iteration, and the final OR.  The function is
-// inlined behind a marker that the build's register audit knows (these waves may use the
-// AGPRs, the compute waves may not); it never returns, the waves end in it.  pidx / tidx are
-// the prefix and tree parts of the unit's index segment, as in the kernel.
+// no rows, so that the compute waves issue none.  Rows pass through these waves' VGPRs
+// (plain non-temporal 16-byte loads, which reach a higher rate from HBM than LDS-DMA
+// gathers) on their way to LDS.  Helper thread hh covers keys hk and hk + 16 of a tile and
+// chunk slot hc of each of the 9 groups.  Two register stages hold tiles t+2 and t+3: each
+// tile's loads go out two iterations before it is written to LDS, so that two tiles are in
+// flight; tiles 0 and 1 start them, from index entries e00 .. e11 that the kernel loaded
+// with its first reads.  checks() takes part in the tree check (its barriers) and says
+// whether the workgroup ends there.  The loop mirrors the compute waves' barriers one for
+// one from then on: the first scores', one per iteration, and the final OR.  The function
+// is inlined behind a marker that the build's register audit knows (these waves may use the
+// AGPRs, the compute waves may not); it never returns, the waves end in it.  pidx / tidx
+// are the prefix and tree parts of the unit's index segment, as in the kernel.
 template <bool kPaged, class Checks>
 [[noreturn]] __device__ __attribute__((always_inline)) inline void gather_helper(const char* pool_in, int64_t row_stride_bytes,
                                                         int64_t pool_slots, int T, int page_log2, int max_page,
@@ -715,12 +717,12 @@ template <bool kPaged, class Checks>
 // kPaged: the prefix is addressed through a block table of 2^page_log2-slot pages (the
 // index segment holds page ids); otherwise through one slot per token.  kBigTree: T > 64,
 // so a row's ancestor mask takes kMaxTreeWords 64-bit words instead of one.  kHelp: at
-// most 64 rows in one M tile, so waves 2 and 3 hold no rows; they gather the tiles
-// (gather_helper) and the compute waves issue none after tiles 0 and 1.  kRG: one M tile of
-// more rows; no other workgroup reads the same keys, so every gather goes to HBM, and the
-// compute waves stage their pieces in VGPRs (plain non-temporal 16-byte loads, which reach a
-// higher rate from HBM than direct-to-LDS loads) and write them to LDS at the end of the
-// iteration.
+// most 64 rows in one M tile, so waves 2 and 3 hold no rows; they gather every tile
+// (gather_helper) and the compute waves issue no gathers.  kRG: one M tile of more rows; no
+// other workgroup reads the same keys, so every gather goes to HBM, and the compute waves
+// stage their pieces in VGPRs (plain non-temporal 16-byte loads, which reach a higher rate
+// from HBM than direct-to-LDS loads) and write them to LDS at the end of the iteration
+// (tiles 0 and 1 too, except for big trees).
 template <bool kPaged, bool kBigTree, bool kHelp, bool kRG>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_partial(PartialArgs a) {
