@@ -382,8 +382,12 @@ def test_split_length_changes_only_rounding(split):
 
 # --------------------------------------------------------------------------- errors
 
-def test_device_errors_poison_only_the_offending_request():
-    cfg = synth.small_config(30, batch=4, prefix=[200, 300, 100, 50], tree_nodes=12, heads=8, slots=4096)
+# 12 nodes x H heads: 48 rows (helper waves gather every tile), 96 rows (register-staged
+# gathers) or 192 rows (two M tiles, LDS-DMA gathers); the bad parent ends the workgroup after
+# the tree check on each path
+@pytest.mark.parametrize("heads", [4, 8, 16])
+def test_device_errors_poison_only_the_offending_request(heads):
+    cfg = synth.small_config(30, batch=4, prefix=[200, 300, 100, 50], tree_nodes=12, heads=heads, slots=4096)
     bad = dict(cfg)
     par = cfg["tree_parent"].copy()
     par[1, 5] = 7  # parent after the node
@@ -406,7 +410,7 @@ def test_device_errors_poison_only_the_offending_request():
             compare(out[rows], lse[rows], ref_out[rows], ref_lse[rows])
     # prefix longer than max_prefix_len
     plens[3] = 301
-    bad2 = synth.small_config(30, batch=4, prefix=list(plens), tree_nodes=12, heads=8, slots=4096)
+    bad2 = synth.small_config(30, batch=4, prefix=list(plens), tree_nodes=12, heads=heads, slots=4096)
     out2, lse2, _ = run_gpu(bad2, v)
     assert v.read_device_errors() == mv.DEVERR_BAD_PREFIX
     assert np.all(np.isnan(out2[3 * t:])) and np.all(np.isfinite(out2[:3 * t]))
