@@ -1472,8 +1472,12 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
 // more units than kSlots * kDepth take further rounds, folded in by an online rescale).  The
 // round's maximum lse, taken over the workgroup, is the reference of the weights; the slots
 // add up through LDS in a fixed order.  A NaN partial lse (a poisoned unit) makes the row NaN.
+// The instantiations with at most 4 column groups and 4 units per slot are held to 64 VGPRs,
+// so that 8 workgroups fit on a CU and a grid of 2,048 runs in one round (at 67 VGPRs the
+// last 256 waited for a second one).
 template <int kSplit, int kPer, int kDepth>
-__global__ __launch_bounds__(256) void k_merge(MergeArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((kSplit <= 4 && kDepth <= 4) ? 8 : 1)))
+void k_merge(MergeArgs a) {
   constexpr int kCols = kVdim / kSplit;   // columns of this workgroup
   constexpr int kLanes = kCols / kPer;    // lanes per unit
   constexpr int kGroups = 64 / kLanes;    // units per wave
