@@ -69,12 +69,39 @@ def algorithmic_counts(cfg: dict) -> dict:
                 prefix_flops=2 * h * t * int(plens.sum()) * (576 + 512))
 
 
+def code_text(src: str) -> str:
+    """C++ source with its comments and whitespace removed (string literals kept), so that an
+    edit of the comments alone does not count as a change of the code."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c == '"' or c == "'":  # a literal, copied whole
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        elif c.isspace():
+            i += 1
+        else:
+            out.append(c)
+            i += 1
+    return "".join(out)
+
+
 def source_hash() -> str:
-    """Short hash of the partial kernel's sources, to tie stored profiler counters to this build."""
+    """Short hash of the partial kernel's sources (code only, see code_text), to tie stored
+    profiler counters to this build."""
     h = hashlib.sha256()
     for f in ("kernels.hip", "mlv_internal.h"):
-        with open(os.path.join(ROOT, "mla_tree_verify_mlaverify_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "mla_tree_verify_mlaverify_amd", "csrc", f), encoding="utf-8") as fh:
+            h.update(code_text(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

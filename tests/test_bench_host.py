@@ -51,6 +51,14 @@ def test_counts_match_ancestor_walk_on_random_batches():
         assert c["prefix_flops"] == 2 * h * t * sum(prefix) * 1088
 
 
+def test_source_hash_ignores_comments_only():
+    src = 'int a = 1;  // the count\n/* block\n comment */ asm("s_nop 1 // kept");\nchar c = \'"\';\n'
+    same = 'int a = 1;\n// another comment\nasm("s_nop 1 // kept");   char c = \'"\';'
+    assert bench.code_text(src) == bench.code_text(same)
+    assert bench.code_text(src) != bench.code_text(src.replace("1;", "2;"))
+    assert bench.code_text(src) != bench.code_text(src.replace("s_nop 1 // kept", "s_nop 2 // kept"))
+
+
 def test_stored_traffic_follows_the_kernel_sources():
     # the committed counters are reported only for the sources they were taken from
     path = os.path.join(ROOT, "profiles", "k_partial_p185000_t64_h8.md")
