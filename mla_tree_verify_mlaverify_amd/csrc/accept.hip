@@ -25,7 +25,7 @@ namespace {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kArgThreads = 256;
-constexpr int kArgChunk = 4096;  // logits per workgroup (16 per thread)
+constexpr int kArgChunk = 8192;  // logits per workgroup (32 per thread)
 
 __device__ __forceinline__ uint64_t arg_key(float v, uint32_t idx) {
   uint32_t u = __float_as_uint(v);
@@ -116,16 +116,16 @@ __global__ __launch_bounds__(kArgThreads) void k_accept_argmax(AcceptArgs a) {
   const int64_t c1 = c0 + kArgChunk < a.vocab ? c0 + kArgChunk : a.vocab;
   const float* lr = a.logits + (int64_t)row * a.vocab;
   uint64_t best = 0ull;
-  if (kVec) {  // vocab % 4 == 0 and 16-byte aligned rows: 4 logits per load, 4 loads in flight
-    for (int64_t i = c0 + 4 * threadIdx.x; i < c1; i += 4 * 4 * kArgThreads) {
-      f32x4 v[4];
+  if (kVec) {  // vocab % 4 == 0 and 16-byte aligned rows: 4 logits per load, 8 loads in flight
+    for (int64_t i = c0 + 4 * threadIdx.x; i < c1; i += 8 * 4 * kArgThreads) {
+      f32x4 v[8];
 #pragma unroll
-      for (int j = 0; j < 4; j++) {
+      for (int j = 0; j < 8; j++) {
         const int64_t e = i + (int64_t)j * 4 * kArgThreads;
         if (e < c1) v[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(lr + e));
       }
 #pragma unroll
-      for (int j = 0; j < 4; j++) {
+      for (int j = 0; j < 8; j++) {
         const int64_t e = i + (int64_t)j * 4 * kArgThreads;
         if (e < c1) {
 #pragma unroll
