@@ -6,7 +6,7 @@
 // argmax of the last row visited is the bonus token.
 //
 // Two launches:
-//   k_accept_argmax one workgroup per (logits row, 4096-logit chunk): the chunk's best
+//   k_accept_argmax one workgroup per (logits row, 8192-logit chunk): the chunk's best
 //                   (value, index) becomes an orderable 64-bit key merged into the row's
 //                   key with one atomic max; the key orders by value (NaN below every
 //                   number, -0 equal to +0), then by lower index, so the atomic max of the
