@@ -695,10 +695,10 @@ template <bool kPaged, class Checks>
     rows(st, tl + 4, en);
     entries(en, tl + 6);
   };
-  // The loop mirrors the compute waves' barriers: the first scores', then one per tile until
-  // the last.  It is unrolled by two, one stage per half, so that every path into its head
-  // leaves the loads in the same order (st0, en0, st1, en1) and the compiler's waits stay
-  // counted.
+  // The loop mirrors the compute waves' barriers after their first scores': one per tile
+  // until the last.  It is unrolled by two, one stage per half, so that every path into its
+  // head leaves the loads in the same order (st0, en0, st1, en1) and the compiler's waits
+  // stay counted.
   for (int t = 0;;) {
     __syncthreads();
     if (t == ntiles) break;
