@@ -26,11 +26,11 @@ def ragged_case(seed, prefix, tree_lens, heads, slots, q_scale=1.0):
                 heads=heads, slots=slots, sm_scale=parts[0]["sm_scale"])
 
 
-def run_ragged(case, max_t=None, split=0, v=None, out_fill=None):
+def run_ragged(case, max_t=None, split=0, v=None, out_fill=None, page_size=0):
     max_t = max_t or int(case["tree_lens"].max())
     v = v or mv.Verifier(num_heads=case["heads"], max_batch=len(case["prefix_lens"]), max_tree_nodes=max_t,
                          max_prefix_len=max(1, int(case["prefix_lens"].max())), pool_slots=case["slots"],
-                         sm_scale=case["sm_scale"], split_tokens=split, device=DEV)
+                         sm_scale=case["sm_scale"], split_tokens=split, page_size=page_size, device=DEV)
     rows = case["q"].shape[0]
     out = torch.full((rows, case["heads"], 512), out_fill if out_fill is not None else float("nan"),
                      dtype=torch.bfloat16, device=DEV)
@@ -53,6 +53,7 @@ def oracle(case):
     (82, [1500, 0, 257, 33, 9000], [64, 5, 1, 17, 33], 8, 256),
     (83, [4000, 100, 2000], [8, 1, 3], 8, 0),                # one M tile: the helper-wave gathers
     (84, [640] * 6, [2, 31, 32, 33, 63, 64], 16, 0),         # tile and M-tile edges
+    (85, [2500, 40, 900], [16, 3, 9], 8, 0),                 # one M tile of 128 rows: register-staged gathers
 ])
 def test_ragged_parity(seed, prefix, tree_lens, heads, split):
     case = ragged_case(seed, prefix, tree_lens, heads, slots=max(4096, 2 * (sum(prefix) + sum(tree_lens))))
@@ -97,3 +98,40 @@ def test_bad_tree_length_poisons_that_request_and_later_ones():
     assert v.read_device_errors() == mv.DEVERR_BAD_TREE_LEN
     compare(out[:4], lse[:4], ref_out, ref_lse)
     assert np.all(out[4:] == 7.0) and np.all(lse[4:] == 7.0)
+
+
+def paged_ragged_case(seed, prefix, tree_lens, heads, slots, page):
+    """The ragged case with its prefixes paged: per request the page ids of its ceil(P_b / page)
+    prefix pages (distinct, below the top quarter of the pool), then its T_b tree slots (top
+    quarter); returned with the same batch addressed one slot per token."""
+    case = ragged_case(seed, prefix, tree_lens, heads, slots)
+    rng = np.random.default_rng(40_000 + seed)
+    top = slots - slots // 4
+    n_pages = [-(-p // page) for p in prefix]
+    pages = rng.choice(top // page, size=sum(n_pages), replace=False)
+    tree = top + rng.choice(slots - top, size=sum(tree_lens), replace=False)
+    segs, flat, pp, tp = [], [], 0, 0
+    for p, t, n in zip(prefix, tree_lens, n_pages):
+        pg, ts = pages[pp:pp + n], tree[tp:tp + t]
+        pos = np.arange(p)
+        segs += [pg, ts]
+        flat += [pg[pos // page] * page + pos % page, ts]
+        pp, tp = pp + n, tp + t
+    paged = dict(case, kv_indices=np.concatenate(segs).astype(np.int32))
+    per_token = dict(case, kv_indices=np.concatenate(flat).astype(np.int32))
+    return paged, per_token
+
+
+@pytest.mark.parametrize("seed,prefix,tree_lens,heads,page", [
+    (90, [700, 0, 2100, 33], [5, 1, 40, 64], 8, 16),   # four M tiles (LDS-DMA gathers)
+    (91, [1300, 257], [9, 3], 8, 64),                    # one M tile of 72 rows (register-staged)
+    (92, [900, 65, 400], [2, 8, 5], 4, 8),               # one M tile of 32 rows (helper waves)
+])
+def test_ragged_paged_equals_its_expansion_and_oracle(seed, prefix, tree_lens, heads, page):
+    paged, flat = paged_ragged_case(seed, prefix, tree_lens, heads, slots=16384, page=page)
+    a, la, v = run_ragged(paged, page_size=page)
+    assert v.read_device_errors() == 0
+    b, lb, _ = run_ragged(flat)
+    assert np.array_equal(a, b) and np.array_equal(la, lb)
+    ref_out, ref_lse = oracle(flat)
+    print(compare(a, la, ref_out, ref_lse))
