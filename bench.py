@@ -525,6 +525,7 @@ def main() -> int:
             per[name]["steps"] = steps
             if var is None:
                 per[name].update(profile_fields(name))
+                per[name]["roofline"]["traffic"] = stored_traffic(name)
             del r, c
             torch.cuda.empty_cache()
         line["per_config"] = per
