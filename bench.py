@@ -20,7 +20,9 @@ prefix, scattered over the lower half of a 524,288-slot pool, into one run in th
 half (the index list is restored before each call, outside the timed region).  With
 --op accept it measures greedy acceptance of a 64-node tree over fp32 logits of a
 131,072-token vocabulary.  With --op gather it runs the scattered-row read probe alone: the
-185k workload's prefix rows read into registers and into LDS at 256-2,048 workgroups.
+185k workload's prefix rows read into registers and into LDS at 256-2,048 workgroups.  With
+--op ragged it times a ragged call (a tree size per request, 4-32 nodes, on the batch of 8)
+against the same batch padded to its largest tree.
 """
 
 from __future__ import annotations
@@ -359,6 +361,174 @@ def bench_accept(args) -> int:
     return 0
 
 
+RAGGED_SEED = 5
+RAGGED_METRIC = ("ragged verify µs/call (a tree size per request) against the same batch padded to its "
+                 "largest tree, 8 requests, 1k-131k prefixes, 16 heads")
+
+
+def ragged_workload(seed: int = RAGGED_SEED):
+    """The batch-of-8 workload (1k-131k prefixes, 32-node trees, 16 heads) with a tree size
+    drawn per request, uniform in 4..32 (the first request keeps all 32, so the padded call
+    has the same largest tree).  A request of T_b nodes keeps the first T_b nodes of its tree
+    (parents precede children, so they form a tree), their query rows and the first T_b tree
+    slots of its index segment.  Returns (the padded workload, the packed ragged arrays)."""
+    from workloads import synth
+
+    cfg = synth.make_config(4)
+    B, T, H = cfg["batch"], cfg["tree_nodes"], cfg["heads"]
+    tl = np.random.default_rng(seed).integers(4, T + 1, size=B).astype(np.int32)
+    tl[0] = T
+    plens = cfg["prefix_lens"].astype(np.int64)
+    offs = synth.request_offsets(plens, T)
+    q = cfg["q"].reshape(B, T, H, -1)
+    rag = dict(
+        q=np.concatenate([q[b, : tl[b]] for b in range(B)]),
+        kv_indices=np.concatenate([cfg["kv_indices"][offs[b]: offs[b] + plens[b] + tl[b]] for b in range(B)]
+                                  ).astype(np.int32),
+        prefix_lens=cfg["prefix_lens"].astype(np.int32),
+        tree_lens=tl,
+        tree_parent=np.concatenate([cfg["tree_parent"][b, : tl[b]] for b in range(B)]).astype(np.int32))
+    return cfg, rag
+
+
+def ragged_counts(cfg: dict, rag: dict) -> dict:
+    """Algorithmic bytes and flops of the ragged call: each request's prefix and its T_b tree
+    keys read once; 2 H (576 + 512) flops per visible (row, key) pair."""
+    from workloads import synth
+
+    h = cfg["heads"]
+    plens = rag["prefix_lens"].astype(np.int64)
+    tl = rag["tree_lens"].astype(np.int64)
+    keys = int(plens.sum() + tl.sum())
+    rows = int(tl.sum())
+    visible, o = 0, 0
+    for b in range(len(tl)):
+        depth = synth.tree_depths(rag["tree_parent"][o: o + tl[b]])
+        visible += int(tl[b] * plens[b]) + int((depth + 1).sum())
+        o += int(tl[b])
+    total = keys * (KV_ROW_BYTES + INDEX_BYTES) + rows * h * (576 * 2 + 512 * 2 + 4)
+    return dict(keys=keys, kv_bytes=keys * KV_ROW_BYTES, total_bytes=total, flops=2 * h * visible * (576 + 512))
+
+
+def bench_ragged(args) -> int:
+    """Times the ragged call (mlaverify_run_ragged) and the padded call (mlaverify_run on the
+    same batch with every request at the largest tree) with the verify protocol: clock settle,
+    warmup, caches flushed before each call, one event pair per call, then the library's
+    per-kernel events."""
+    import torch
+
+    import mla_tree_verify_mlaverify_amd as mv
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg, rag = ragged_workload()
+    B, T, H = cfg["batch"], cfg["tree_nodes"], cfg["heads"]
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def i32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+
+    pool = bf16(cfg["pool"])
+    plens = i32(cfg["prefix_lens"])
+    v = mv.Verifier(num_heads=H, max_batch=B, max_tree_nodes=T, max_prefix_len=int(cfg["prefix_lens"].max()),
+                    pool_slots=cfg["slots"], sm_scale=cfg["sm_scale"], device=dev)
+    flush = torch.zeros(1 << 28, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    pq, pidx, ppar = bf16(cfg["q"]), i32(cfg["kv_indices"]), i32(cfg["tree_parent"])
+    pout = torch.empty((B * T, H, 512), dtype=torch.bfloat16, device=dev)
+    plse = torch.empty((B * T, H), dtype=torch.float32, device=dev)
+    rows = int(rag["tree_lens"].sum())
+    rq, ridx, rtl, rpar = bf16(rag["q"]), i32(rag["kv_indices"]), i32(rag["tree_lens"]), i32(rag["tree_parent"])
+    rout = torch.empty((rows, H, 512), dtype=torch.bfloat16, device=dev)
+    rlse = torch.empty((rows, H), dtype=torch.float32, device=dev)
+
+    def padded():
+        v.run(pq, pool, pidx, plens, ppar, out=pout, lse=plse, stream=stream)
+
+    def ragged():
+        v.run_ragged(rq, pool, ridx, plens, rtl, rpar, T, out=rout, lse=rlse, stream=stream)
+
+    res = {}
+    for name, step in (("ragged", ragged), ("padded", padded)):
+        settle(step, flush, args.warm)
+        for _ in range(args.warmup):
+            if not args.warm:
+                flush.add_(1.0)
+            step()
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for k in range(args.steps):
+            if not args.warm:
+                flush.add_(1.0)
+            starts[k].record(stream)
+            step()
+            ends[k].record(stream)
+        torch.cuda.synchronize()
+        call_ms = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+        v.profile_begin(args.steps)
+        for _ in range(args.steps):
+            if not args.warm:
+                flush.add_(1.0)
+            step()
+        torch.cuda.synchronize()
+        kms = v.profile_end()
+        res[name] = dict(call_ms=call_ms, med=statistics.median(call_ms),
+                         part=sum(k[0] for k in kms) / len(kms), merge=sum(k[1] for k in kms) / len(kms))
+    assert v.read_device_errors() == 0
+    # the ragged rows equal the padded call's rows of the nodes they keep (bit for bit: the
+    # plan differs, so only up to the partials' rounding)
+    o = 0
+    worst = 0.0
+    for b in range(B):
+        t_b = int(rag["tree_lens"][b])
+        d = (rout[o: o + t_b].float() - pout[b * T: b * T + t_b].float()).abs().max().item()
+        worst = max(worst, d)
+        o += t_b
+    rc = ragged_counts(cfg, rag)
+    pc = algorithmic_counts(cfg)
+
+    def summary(r, counts):
+        t_hbm = counts["total_bytes"] / (HBM_PEAK_GBS * 1e9)
+        t_mfma = counts["flops"] / (BF16_MFMA_PEAK_TFLOPS * 1e12)
+        part_s = r["part"] * 1e-3
+        if t_mfma >= t_hbm:
+            ach = counts["flops"] / part_s / 1e12
+            roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(ach / BF16_MFMA_PEAK_TFLOPS, 4)}
+        else:
+            ach = counts["total_bytes"] / part_s / 1e9
+            roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(ach / HBM_PEAK_GBS, 4)}
+        roof.update(traffic=None, kernel="k_partial", kernel_avg_us=round(r["part"] * 1e3, 2))
+        return {"us_per_call": {"median": round(r["med"] * 1e3, 2),
+                                "p10": round(float(np.percentile(r["call_ms"], 10)) * 1e3, 2),
+                                "p90": round(float(np.percentile(r["call_ms"], 90)) * 1e3, 2)},
+                "kernels_us": {"partial": round(r["part"] * 1e3, 2), "merge": round(r["merge"] * 1e3, 2)},
+                "kv_gbs": round(counts["kv_bytes"] / (r["med"] * 1e-3) / 1e9, 2),
+                "gflop": round(counts["flops"] / 1e9, 2), "roofline": roof}
+
+    rs, ps = summary(res["ragged"], rc), summary(res["padded"], pc)
+    line = {
+        "metric": RAGGED_METRIC, "value": rs["us_per_call"]["median"], "unit": "us/call", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(res["ragged"]["med"], 5),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"ragged_b{B}_ploguniform_t4to{T}_h{H}", "batch": B, "heads": H,
+                   "tree_lens": [int(x) for x in rag["tree_lens"]],
+                   "prefix_lens": [int(x) for x in cfg["prefix_lens"]],
+                   "cache": "warm" if args.warm else "flushed 1 GiB before each call"},
+        "ragged": rs, "padded": ps,
+        "speedup_vs_padded": round(res["padded"]["med"] / res["ragged"]["med"], 3),
+        "rows": {"ragged": rows * H, "padded": B * T * H},
+        "max_abs_diff_vs_padded_rows": worst,
+        "roofline": rs["roofline"],
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 GATHER_METRIC = "scattered KV-row gather GB/s (185,000 rows of 1,152 B from a 262,144-slot pool, caches flushed)"
 GATHER_GRIDS = (256, 512, 1024, 2048)
 
@@ -452,7 +622,7 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--split", type=int, default=0, help="fixed split length (0 = automatic)")
-    ap.add_argument("--op", choices=("verify", "relocate", "accept", "gather"), default="verify")
+    ap.add_argument("--op", choices=("verify", "relocate", "accept", "gather", "ragged"), default="verify")
     ap.add_argument("--page", type=int, default=0, help="prefix page size (block table of page ids); 0 = per token")
     ap.add_argument("--no-per-config", action="store_true",
                     help="time only the chosen workload (by default the 185k run also times every other one)")
@@ -466,6 +636,8 @@ def main() -> int:
         return bench_accept(args)
     if args.op == "gather":
         return bench_gather(args)
+    if args.op == "ragged":
+        return bench_ragged(args)
 
     import torch
 

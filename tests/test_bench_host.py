@@ -96,3 +96,40 @@ def test_every_package_name_the_bench_calls_exists():
     assert names and "probe_gather" in names
     missing = sorted(n for n in names if not hasattr(mv, n))
     assert not missing, missing
+
+
+def test_ragged_workload_is_a_truncation_of_the_batch():
+    cfg, rag = bench.ragged_workload()
+    B, T, H = cfg["batch"], cfg["tree_nodes"], cfg["heads"]
+    tl = rag["tree_lens"]
+    assert tl[0] == T and tl.min() >= 4 and tl.max() <= T
+    assert rag["q"].shape == (int(tl.sum()), H, 576)
+    offs = synth.request_offsets(cfg["prefix_lens"], T)
+    o, r = 0, 0
+    for b in range(B):
+        p, t = int(cfg["prefix_lens"][b]), int(tl[b])
+        # the request's prefix entries and its first t tree entries, in order
+        assert np.array_equal(rag["kv_indices"][o: o + p + t], cfg["kv_indices"][offs[b]: offs[b] + p + t])
+        par = rag["tree_parent"][r: r + t]
+        assert np.array_equal(par, cfg["tree_parent"][b, :t])
+        assert all(-1 <= par[i] < i for i in range(t))
+        assert np.array_equal(rag["q"][r: r + t], cfg["q"].reshape(B, T, H, 576)[b, :t])
+        o += p + t
+        r += t
+    assert o == len(rag["kv_indices"])
+
+
+def test_ragged_counts_equal_the_padded_counts_at_full_trees():
+    # with every request at the full tree, the ragged call is the padded one: same keys, flops
+    cfg, _ = bench.ragged_workload()
+    B, T = cfg["batch"], cfg["tree_nodes"]
+    full = dict(prefix_lens=cfg["prefix_lens"].astype(np.int32), tree_lens=np.full(B, T, np.int32),
+                tree_parent=cfg["tree_parent"].reshape(-1))
+    rc, pc = bench.ragged_counts(cfg, full), bench.algorithmic_counts(cfg)
+    assert rc["flops"] == pc["flops"] and rc["kv_bytes"] == pc["kv_bytes"]
+    assert rc["total_bytes"] == pc["total_bytes"]
+    # and one node fewer in request 0 removes exactly that node's visible keys
+    less = dict(full, tree_lens=np.array([T - 1] + [T] * (B - 1), np.int32),
+                tree_parent=np.concatenate([cfg["tree_parent"][0, : T - 1], cfg["tree_parent"][1:].reshape(-1)]))
+    seen = visible_counts(list(cfg["tree_parent"][0]), int(cfg["prefix_lens"][0]))[T - 1]
+    assert pc["flops"] - bench.ragged_counts(cfg, less)["flops"] == 2 * cfg["heads"] * seen * 1088
