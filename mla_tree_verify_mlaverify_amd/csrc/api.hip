@@ -5,6 +5,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 #include <new>
 #include <vector>
@@ -47,9 +48,12 @@ Layout layout_for(const mlaverify_config& c) {
   int units_cap = 0;
   int64_t rows_cap = 0;
   for (int T = 1; T <= c.max_tree_nodes; T++) {
+    // a ragged call may split a request into up to n_mt times as many units, of at most one
+    // M tile each (ragged_caps)
     const int u = units_for(c, c.max_batch, T);
-    if (u > units_cap) units_cap = u;
-    const int64_t rows = (int64_t)u * c.num_heads * T;
+    const int n_mt = mtiles_for(c.num_heads, T);
+    if (u * n_mt > units_cap) units_cap = u * n_mt;
+    const int64_t rows = std::max((int64_t)u * c.num_heads * T, (int64_t)u * n_mt * kRowsPerBlock);
     if (rows > rows_cap) rows_cap = rows;
   }
   L.units_cap = units_cap;
@@ -167,7 +171,12 @@ int enqueue_run(const mlaverify_config& c, const RunAreas& w, int batch, int T, 
   ka.split_fixed = c.split_tokens;
   ka.target_units = target_units_for(n_mt);
   ka.min_split = kMinSplit;
-  ka.units_cap = units_grid;
+  // Bounds of the unit table and the partial rows.  With one tree size the plan makes at
+  // most units_grid units of M rows.  A ragged call weighs each unit by the M tiles its
+  // request fills and keeps the weighted count within n_mt * units_grid (the grid), so it
+  // makes at most that many units, each of at most kRowsPerBlock rows per M tile.
+  ka.units_cap = tree_lens ? n_mt * units_grid : units_grid;
+  ka.rows_cap = tree_lens ? n_mt * units_grid * kRowsPerBlock : units_grid * M;
   ka.scale_log2 = c.sm_scale * 1.4426950408889634f;
   ka.flags = c.flags;
   ka.page_log2 = page_log2(c.page_size);
@@ -183,7 +192,7 @@ int enqueue_run(const mlaverify_config& c, const RunAreas& w, int batch, int T, 
   ma.batch = batch;
   ma.H = c.num_heads;
   ma.M = M;
-  ma.units_cap = units_grid;
+  ma.rows_cap = ka.rows_cap;
   // units of one request, as the plan is expected to make them: under an automatic split the
   // target count shared by the batch (longer requests take more of them, in more rounds)
   ma.units_hint = c.split_tokens > 0 ? (int)(c.max_prefix_len > 0 ? cdiv(c.max_prefix_len, c.split_tokens) : 1)

@@ -318,11 +318,21 @@ __device__ int wg_exclusive_scan(int v, int* s_tmp, int& total) {
 //     first_unit_b = exclusive scan of units_b.
 // Fills s_unit[] for unit g (request, key offset, P, first unit, units, error bits, S, T_b,
 // node offset) and returns the number of units.  The publishing workgroup also writes the
-// plan out.
+// plan out.  (It serves batches over 64 requests; a ragged one is then planned as if every
+// request had the call's largest tree, which keeps each request's partial rows apart.)
 struct UnitPlan {
   int b, key_off, prefix, first, units, split, tree_nodes, node_off, total;
+  int g, mt, prow;  // a ragged plan's unit and M tile for the workgroup (g < 0: no work), first partial row
   uint32_t err;
 };
+
+// Ragged calls deal their work items (unit, M tile), the M tiles of a unit consecutive, to
+// the XCDs in equal contiguous ranges, so that a unit's M tiles share an XCD and its L2 and
+// no XCD gets more than its share.  Workgroup bid's item, or `items` when it has none.
+__device__ __forceinline__ int ragged_item(int bid, int items) {
+  const int per = (items + 7) >> 3, s = bid >> 3;
+  return s < per ? min((bid & 7) * per + s, items) : items;
+}
 
 // Entries of a prefix of p tokens in its index segment: one per page of 2^page_log2 slots.
 __device__ __forceinline__ int seg_entries(int p, int page_log2) { return (p + (1 << page_log2) - 1) >> page_log2; }
@@ -476,7 +486,7 @@ __device__ int plan_units(const PartialArgs& a, int g, bool publish, int* s_tmp,
         rp.err = err[j];
         rp.tree_nodes = tl[j];
         rp.node_off = node_off;
-        rp.pad = 0;
+        rp.prow = first * a.M;
         a.req[i] = rp;
       }
       key_off += seg_entries(pv[j], a.page_log2) + tl[j];
@@ -512,8 +522,15 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
 // uniformly over the workgroup, when the batch needs plan_units instead: more than 64
 // requests, or ragged requests whose unit count rounds past the target (the split search).
 // Fills up for unit g; a publishing wave writes the plan out.
+// A ragged call (a tree size per request) is planned by M tiles: request b fills
+// mt_b = ceil(H T_b / 128) of them, each unit of it takes mt_b workgroups, and the split is
+// the smallest (multiple of 32, at least min_split) for which sum_b mt_b units_b stays
+// within the launch's workgroup budget (target_units x M tiles), so that requests with
+// fewer rows get shorter units instead of idle workgroups.  The workgroup's (unit, M tile)
+// then comes from its item (ragged_item), and the partial rows of request b are packed at
+// prow_b = sum_{b' < b} units_b' H T_b'.
 template <class Hook>
-__device__ bool plan_wave(const PartialArgs& a, int g, bool publish, UnitPlan& up, Hook&& after_loads) {
+__device__ bool plan_wave(const PartialArgs& a, int bid, int g, bool publish, UnitPlan& up, Hook&& after_loads) {
   const int B = a.batch, T = a.T;
   if (B > 64) {
     after_loads();
@@ -537,18 +554,55 @@ __device__ bool plan_wave(const PartialArgs& a, int g, bool publish, UnitPlan& u
   const int seg = in ? seg_entries(pv, a.page_log2) + tl : 0;
   const int seg_inc = wave_incl_scan(seg);
   const int node_inc = wave_incl_scan(tl);
+  const bool ragged = a.tree_lens != nullptr;
+  // workgroups per unit of this request (a request without rows keeps one, for its bookkeeping)
+  const int mtw = !in ? 0 : ragged ? max(1, (a.H * tl + kRowsPerBlock - 1) / kRowsPerBlock) : a.n_mtiles;
+  auto units_at = [&](int s) { return in ? max(1, min((pv + tk + s - 1) / s, (pv + s - 1) / s + 1)) : 0; };
   int S = a.split_fixed;
-  if (!fixed_split) {
+  if (!fixed_split && !ragged) {
     const int work = __builtin_amdgcn_readlane(wave_incl_scan(pv + tk), 63);
     const int U = a.target_units;
     S = max(a.min_split, ((work + U - 1) / U + kTileKeys - 1) / kTileKeys * kTileKeys);
+  } else if (!fixed_split) {
+    // 32-bit arithmetic (64-bit division here costs the kernel registers); a weighted sum
+    // that could pass 2^31 goes to plan_units instead.  With one tree size every weight is
+    // the same and this is the split of a call without tree sizes.
+    const int budget = a.target_units * a.n_mtiles;
+    float wf = (float)(pv + tk) * (float)mtw;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) wf += __shfl_xor(wf, off, 64);
+    if (__builtin_amdgcn_readfirstlane(__float_as_uint(wf)) > __float_as_uint(1.0e9f)) return false;
+    const int work = __builtin_amdgcn_readlane(wave_incl_scan((pv + tk) * mtw), 63);
+    const int sum_mt = __builtin_amdgcn_readlane(wave_incl_scan(mtw), 63);
+    auto round_up = [](int x) { return (x + kTileKeys - 1) / kTileKeys * kTileKeys; };
+    auto items_at = [&](int s) { return __builtin_amdgcn_readlane(wave_incl_scan(units_at(s) * mtw), 63); };
+    S = max(a.min_split, round_up((work + budget - 1) / budget));
+    if (items_at(S) > budget && sum_mt < budget) {
+      // sum_b mt_b units_b <= sum_b mt_b ((P_b + tkeys_b) / s + 1), so s = ceil(work /
+      // (budget - sum mt_b)) fits; bisect for the smallest fitting multiple of 32 (the count
+      // does not grow with s)
+      int lo = S + kTileKeys;
+      int hi = max(lo, max(a.min_split, round_up((work + (budget - sum_mt) - 1) / (budget - sum_mt))));
+      while (lo < hi) {
+        const int mid = (lo + hi) / 2 / kTileKeys * kTileKeys;
+        if (items_at(mid) <= budget) hi = mid; else lo = mid + kTileKeys;
+      }
+      S = hi;
+    }
   }
-  const int units = in ? max(1, min((pv + tk + S - 1) / S, (pv + S - 1) / S + 1)) : 0;
+  const int units = units_at(S);
   const int first_inc = wave_incl_scan(units);
   const int total = __builtin_amdgcn_readlane(first_inc, 63);
-  if (!fixed_split && total > a.target_units && B < a.target_units) return false;
+  if (!fixed_split && !ragged && total > a.target_units && B < a.target_units) return false;
   const int first = first_inc - units;
-  const uint64_t mine = __ballot(in && g >= first && g < first_inc);
+  int item = 0, item_inc = 0, prow_inc = 0;
+  if (ragged) {
+    item_inc = wave_incl_scan(units * mtw);
+    item = ragged_item(bid, __builtin_amdgcn_readlane(item_inc, 63));
+    prow_inc = wave_incl_scan(units * a.H * tl);
+  }
+  const uint64_t mine =
+      __ballot(in && (ragged ? item >= item_inc - units * mtw && item < item_inc : g >= first && g < first_inc));
   up.split = S;
   up.total = total;
   if (mine) {
@@ -565,6 +619,20 @@ __device__ bool plan_wave(const PartialArgs& a, int g, bool publish, UnitPlan& u
     up.b = up.key_off = up.prefix = up.first = up.units = up.tree_nodes = up.node_off = 0;
     up.err = 0;
   }
+  // (assigned once: stores to the struct in both arms above get merged through a pointer
+  // select, which would keep it in private memory)
+  int ug = g, umt = 0, uprow = up.first * a.M;
+  if (ragged) {
+    const int l = mine ? __builtin_ctzll(mine) : 0;
+    const int k = item - __builtin_amdgcn_readlane(item_inc - units * mtw, l);
+    const int m = max(1, __builtin_amdgcn_readlane(mtw, l));
+    ug = mine ? up.first + k / m : -1;
+    umt = k % m;
+    uprow = __builtin_amdgcn_readlane(prow_inc - units * a.H * tl, l);
+  }
+  up.g = ug;
+  up.mt = umt;
+  up.prow = uprow;
   if (publish) {
     if (in) {
       ReqPlan rp;
@@ -575,7 +643,7 @@ __device__ bool plan_wave(const PartialArgs& a, int g, bool publish, UnitPlan& u
       rp.err = err;
       rp.tree_nodes = tl;
       rp.node_off = node_inc - tl;
-      rp.pad = 0;
+      rp.prow = ragged ? prow_inc - units * a.H * tl : first * a.M;
       a.req[lane] = rp;
     }
     if (lane == 0) {
@@ -743,15 +811,17 @@ void k_partial(PartialArgs a) {
   // Workgroup -> (unit, M tile).  Consecutive workgroups go to consecutive XCDs, so the M
   // tiles of one unit are given ids that are equal mod 8: they share an XCD and its L2.
   // With fewer than 8 units that would leave XCDs idle; the M tiles then go round-robin.
+  // A ragged call takes its (unit, M tile) from the plan instead (ragged_item).
   const int bid = blockIdx.x;
-  int mt, g;
+  const bool ragged = a.tree_lens != nullptr;
+  int mt0, g0;
   if (a.group_xcd) {
     const int slot = bid >> 3;
-    mt = slot % a.n_mtiles;
-    g = (slot / a.n_mtiles) * 8 + (bid & 7);
+    mt0 = slot % a.n_mtiles;
+    g0 = (slot / a.n_mtiles) * 8 + (bid & 7);
   } else {
-    mt = bid % a.n_mtiles;
-    g = bid / a.n_mtiles;
+    mt0 = bid % a.n_mtiles;
+    g0 = bid / a.n_mtiles;
   }
   // Workgroup 0's first wave samples the shader-cycle and wall-clock counters at its start and
   // end, for the plan readback (the shader clock under load).
@@ -780,10 +850,11 @@ void k_partial(PartialArgs a) {
   };
   // (tile buffer 0 is the plan's scratch: no gather writes it before the plan is done)
   UnitPlan up;
-  const bool planned = plan_wave(a, g, g == 0 && mt == 0 && wu == 0, up, prefetch_q);
+  const bool pub = ragged ? bid == 0 : (g0 == 0 && mt0 == 0);  // the workgroup that publishes the plan
+  const bool planned = plan_wave(a, bid, g0, pub && wu == 0, up, prefetch_q);
   asm volatile("" ::"v"(qpf0), "v"(qpf1));  // the touches have landed (none in flight at any return)
   if (!planned) {
-    up.total = plan_units(a, g, g == 0 && mt == 0, s_tmp, s_unit, reinterpret_cast<int*>(smem));
+    up.total = plan_units(a, g0, pub, s_tmp, s_unit, reinterpret_cast<int*>(smem));
     up.b = s_unit[0];
     up.key_off = s_unit[1];
     up.prefix = s_unit[2];
@@ -794,7 +865,12 @@ void k_partial(PartialArgs a) {
     up.tree_nodes = s_unit[7];
     up.node_off = s_unit[8];
   }
-  if (g >= up.total || g >= a.units_cap) return;
+  // a ragged plan by M tiles names the workgroup's unit and M tile; otherwise its id does
+  const bool by_items = planned && ragged;
+  const int g = by_items ? up.g : g0, mt = by_items ? up.mt : mt0;
+  const int prow = planned ? up.prow : up.first * a.M;
+  __builtin_amdgcn_sched_barrier(0);  // keep the plan's code apart from the unit's
+  if (g < 0 || g >= up.total || g >= a.units_cap) return;
   const int key_off = up.key_off;
   const int prefix = up.prefix;
   const int first_unit = up.first;
@@ -805,6 +881,9 @@ void k_partial(PartialArgs a) {
   const int node_off = up.node_off;  // its first row (node) in q / out / tree_parent
   const int Mb = a.H * Tb;         // its query rows
   const int u = g - first_unit;
+  // The unit's partial rows: prow_u + r for its Mb query rows (never past the buffers)
+  const int prow_u = prow + u * Mb;  // < rows_cap < 2^31
+  if (prow < 0 || prow_u > a.rows_cap - Mb) return;
   const int kbeg = u * S;
   const int npk = max(0, min(S, prefix - kbeg));  // prefix keys of this unit
   const int npt = (npk + kTileKeys - 1) / kTileKeys;
@@ -950,7 +1029,7 @@ void k_partial(PartialArgs a) {
     }
   };
   auto poison = [&]() {  // poisoned request: NaN partials, which the merge turns into NaN rows
-    if (rvalid && h == 0) a.part_lse[(size_t)g * a.M + r] = __uint_as_float(0x7FC00000u);
+    if (rvalid && h == 0) a.part_lse[prow_u + r] = __uint_as_float(0x7FC00000u);
   };
   if (!plan_ok) {
     if (last) masks();  // its parents are still checked and reported
@@ -1418,7 +1497,7 @@ void k_partial(PartialArgs a) {
     // Partials leave as bf16 (each value rounded on its own, like the probabilities fed to
     // the PV MFMAs).  Lane pairs (lrow, h = 0/1) exchange 8-byte groups so that each lane
     // stores 8 consecutive columns.
-    uint16_t* po = a.part_o + ((size_t)g * a.M + r) * kVdim + 8 * h;
+    uint16_t* po = a.part_o + (size_t)(prow_u + r) * kVdim + 8 * h;
 #pragma unroll
     for (int db = 0; db < 16; db++) {
       float X[16];
@@ -1451,7 +1530,7 @@ void k_partial(PartialArgs a) {
         *reinterpret_cast<u32x4*>(po + 32 * db + 16 * p) = v;
       }
     }
-    if (h == 0) a.part_lse[(size_t)g * a.M + r] = lse2;
+    if (h == 0) a.part_lse[prow_u + r] = lse2;
   }
 }
 
@@ -1498,13 +1577,14 @@ void k_merge(MergeArgs a) {
   const int cl = lane % kLanes, slot = w * kGroups + lane / kLanes;
   const int b = row / a.M, r = row - b * a.M;
   ReqPlan R = a.req[b];
-  if (r >= R.tree_nodes * a.H) return;  // past this request's rows (ragged trees)
+  const int Mb = R.tree_nodes * a.H;  // the request's rows, and the row stride of its partials
+  if (r >= Mb) return;  // past this request's rows (ragged trees)
   const size_t orow = (size_t)R.node_off * a.H + r;  // the row in out / lse
-  R.first_unit = min(max(R.first_unit, 0), a.units_cap);  // never index past the partial buffers
-  R.units = min(R.units, a.units_cap - R.first_unit);
-  const float* pl = a.part_lse + (size_t)R.first_unit * a.M + r;
-  const uint16_t* pob = a.part_o + ((size_t)R.first_unit * a.M + r) * kVdim + c0 + kPer * cl;
-  const size_t ustride = (size_t)a.M * kVdim;
+  const int64_t prow = min(max((int64_t)R.prow, (int64_t)0), (int64_t)a.rows_cap);  // never index past
+  R.units = (int)min((int64_t)R.units, ((int64_t)a.rows_cap - prow) / Mb);          // the partial buffers
+  const float* pl = a.part_lse + prow + r;
+  const uint16_t* pob = a.part_o + (size_t)(prow + r) * kVdim + c0 + kPer * cl;
+  const size_t ustride = (size_t)Mb * kVdim;
   float m = -INFINITY, z = 0.f;
   fv acc = {};
   for (int k0 = slot; k0 - slot < R.units; k0 += kDepth * kSlots) {  // rounds (uniform over the workgroup)
@@ -1514,7 +1594,7 @@ void k_merge(MergeArgs a) {
 #pragma unroll
     for (int k = 0; k < kDepth; k++) {
       const int u = min(k0 + k * kSlots, R.units - 1);
-      lu[k] = pl[(size_t)u * a.M];
+      lu[k] = pl[(size_t)u * Mb];
       o[k] = *reinterpret_cast<const hv*>(pob + u * ustride);
     }
     float mr = -INFINITY;

@@ -59,7 +59,7 @@ struct ReqPlan {
   uint32_t err;         // prefix-length / tree-length error bits of this request
   int32_t tree_nodes;   // T_b (0 when a tree length at or before this request is invalid)
   int32_t node_off;     // first row (node) of the request in q / out / lse / tree_parent
-  int32_t pad;
+  int32_t prow;         // first partial row of its unit 0; unit u's rows start at prow + u * H * T_b
 };
 static_assert(sizeof(ReqPlan) == 32, "ReqPlan size");
 
@@ -72,14 +72,15 @@ struct PartialArgs {
   const int32_t* tree_lens;  // [batch] per-request tree sizes T_b <= T, or null: every request has T
   PlanHeader* hdr;       // plan published by workgroup 0 (for the merge and readback)
   ReqPlan* req;
-  uint16_t* part_o;      // [units, M, 512] unit-normalised partial outputs (bf16 bits)
-  float* part_lse;       // [units, M] log2-domain lse of each partial (NaN: poisoned)
+  uint16_t* part_o;      // [rows_cap, 512] unit-normalised partial outputs (bf16 bits), H * T_b rows per unit
+  float* part_lse;       // [rows_cap] log2-domain lse of each partial row (NaN: poisoned)
   int32_t* unit_fast;    // [units] 1 if the unit's prefix was read as one contiguous run
   uint32_t* sticky_err;
   int64_t pool_slots;
   int64_t row_stride_bytes;
   int32_t batch, T, H, M, n_mtiles;  // T: the call's largest tree, M = H * T rows per unit
-  int32_t max_prefix, split_fixed, target_units, min_split, units_cap;
+  int32_t max_prefix, split_fixed, target_units, min_split, units_cap;  // units_cap: entries of unit_fast
+  int32_t rows_cap;      // rows of part_o / part_lse
   float scale_log2;      // sm_scale * log2(e), > 0
   uint32_t flags;
   int32_t page_log2;     // prefix pages of 2^page_log2 slots (0: one slot per token)
@@ -93,7 +94,8 @@ struct MergeArgs {
   const float* part_lse;
   uint16_t* out;
   float* lse;
-  int32_t batch, H, M, units_cap;  // M = H * (the call's largest T): the partials' row stride
+  int32_t batch, H, M;   // M = H * (the call's largest T): rows of a request in out / lse
+  int32_t rows_cap;      // rows of part_o / part_lse
   int32_t units_hint;              // units of one request the plan is expected to make (sizes the merge's rounds)
 };
 

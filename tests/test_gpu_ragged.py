@@ -47,6 +47,40 @@ def oracle(case):
                                        case["tree_lens"], case["tree_parent"], case["sm_scale"])
 
 
+def expected_ragged_plan(prefix, tree_lens, heads, split):
+    """The split and units the ragged plan must choose (at most 64 requests): request b fills
+    mt_b = ceil(H T_b / 128) M tiles and each of its units takes mt_b workgroups; under an
+    automatic split the length is the smallest multiple of 32, at least 128 and at least
+    ceil(sum_b mt_b (P_b + tkeys_b) / budget), whose weighted unit count fits the budget of
+    ceil(256 / M tiles) x M tiles workgroups (when the batch allows)."""
+    cdiv = lambda x, y: -(-x // y)
+    n_mt = cdiv(heads * max(tree_lens), 128)
+    budget = cdiv(256, n_mt) * n_mt
+    mt = [max(1, cdiv(heads * t, 128)) for t in tree_lens]
+    tk = [0 if split else cdiv(t, 32) * 32 for t in tree_lens]
+    units_at = lambda s: [max(1, min(cdiv(p + k, s), cdiv(p, s) + 1)) for p, k in zip(prefix, tk)]
+    items_at = lambda s: sum(u * m for u, m in zip(units_at(s), mt))
+    if split:
+        return split, units_at(split)
+    work = sum((p + k) * m for p, k, m in zip(prefix, tk, mt))
+    s = max(128, cdiv(cdiv(work, budget), 32) * 32)
+    if items_at(s) > budget and sum(mt) < budget:
+        s += 32
+        while items_at(s) > budget:
+            s += 32
+    return s, units_at(s)
+
+
+def check_ragged_plan(v, case, split):
+    s, units = expected_ragged_plan([int(p) for p in case["prefix_lens"]], [int(t) for t in case["tree_lens"]],
+                                    case["heads"], split)
+    plan = v.read_plan()
+    assert plan["split_len"] == s
+    assert [r["units"] for r in plan["requests"]] == units
+    assert [r["first_unit"] for r in plan["requests"]] == list(np.cumsum([0] + units[:-1]))
+    assert plan["total_units"] == sum(units)
+
+
 @pytest.mark.parametrize("seed,prefix,tree_lens,heads,split", [
     (80, [3000, 1, 700, 4096], [1, 5, 64, 200], 8, 0),     # big-tree launch (max 200): four mask words
     (81, [1500, 0, 257, 33, 9000], [64, 5, 1, 17, 33], 8, 0),
@@ -61,6 +95,7 @@ def test_ragged_parity(seed, prefix, tree_lens, heads, split):
     assert v.read_device_errors() == 0
     ref_out, ref_lse = oracle(case)
     print(compare(out, lse, ref_out, ref_lse))
+    check_ragged_plan(v, case, split)
 
 
 def test_ragged_with_equal_trees_is_run_bit_for_bit():
