@@ -193,6 +193,7 @@ int enqueue_run(const mlaverify_config& c, const RunAreas& w, int batch, int T, 
   ma.H = c.num_heads;
   ma.M = M;
   ma.rows_cap = ka.rows_cap;
+  ma.ragged = tree_lens ? 1 : 0;
   // units of one request, as the plan is expected to make them: under an automatic split the
   // target count shared by the batch (longer requests take more of them, in more rounds)
   ma.units_hint = c.split_tokens > 0 ? (int)(c.max_prefix_len > 0 ? cdiv(c.max_prefix_len, c.split_tokens) : 1)

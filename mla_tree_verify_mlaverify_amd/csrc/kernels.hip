@@ -529,7 +529,7 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
 // fewer rows get shorter units instead of idle workgroups.  The workgroup's (unit, M tile)
 // then comes from its item (ragged_item), and the partial rows of request b are packed at
 // prow_b = sum_{b' < b} units_b' H T_b'.
-template <class Hook>
+template <bool kRagged, class Hook>
 __device__ bool plan_wave(const PartialArgs& a, int bid, int g, bool publish, UnitPlan& up, Hook&& after_loads) {
   const int B = a.batch, T = a.T;
   if (B > 64) {
@@ -554,7 +554,7 @@ __device__ bool plan_wave(const PartialArgs& a, int bid, int g, bool publish, Un
   const int seg = in ? seg_entries(pv, a.page_log2) + tl : 0;
   const int seg_inc = wave_incl_scan(seg);
   const int node_inc = wave_incl_scan(tl);
-  const bool ragged = a.tree_lens != nullptr;
+  constexpr bool ragged = kRagged;
   // workgroups per unit of this request (a request without rows keeps one, for its bookkeeping)
   const int mtw = !in ? 0 : ragged ? max(1, (a.H * tl + kRowsPerBlock - 1) / kRowsPerBlock) : a.n_mtiles;
   auto units_at = [&](int s) { return in ? max(1, min((pv + tk + s - 1) / s, (pv + s - 1) / s + 1)) : 0; };
@@ -793,7 +793,7 @@ template <bool kPaged, class Checks>
 // stage their pieces in VGPRs (plain non-temporal 16-byte loads, which reach a higher rate
 // from HBM than direct-to-LDS loads) and write them to LDS at the end of the iteration
 // (tiles 0 and 1 too, except for big trees).
-template <bool kPaged, bool kBigTree, bool kHelp, bool kRG>
+template <bool kPaged, bool kBigTree, bool kHelp, bool kRG, bool kRagged>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_partial(PartialArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[kTileBufs * kTileBytes + kWaves * kQLdsBytes];
@@ -813,7 +813,7 @@ void k_partial(PartialArgs a) {
   // With fewer than 8 units that would leave XCDs idle; the M tiles then go round-robin.
   // A ragged call takes its (unit, M tile) from the plan instead (ragged_item).
   const int bid = blockIdx.x;
-  const bool ragged = a.tree_lens != nullptr;
+  constexpr bool ragged = kRagged;  // the call has a tree size per request
   int mt0, g0;
   if (a.group_xcd) {
     const int slot = bid >> 3;
@@ -837,7 +837,7 @@ void k_partial(PartialArgs a) {
   // in flight.  Ragged calls (Q size known only from the plan) and large Q skip it.
   uint32_t qpf0 = 0, qpf1 = 0;
   auto prefetch_q = [&]() {
-    const int64_t qbytes = a.tree_lens ? 0 : (int64_t)a.batch * a.M * kRowBytes;
+    const int64_t qbytes = kRagged ? 0 : (int64_t)a.batch * a.M * kRowBytes;
     const int xwg = ((int)gridDim.x - (bid & 7) + 7) >> 3;  // workgroups on this XCD
     const int64_t nl = (qbytes + 127) >> 7;
     const int64_t l0 = nl * (bid >> 3) / xwg, l1 = nl * ((bid >> 3) + 1) / xwg;
@@ -851,7 +851,7 @@ void k_partial(PartialArgs a) {
   // (tile buffer 0 is the plan's scratch: no gather writes it before the plan is done)
   UnitPlan up;
   const bool pub = ragged ? bid == 0 : (g0 == 0 && mt0 == 0);  // the workgroup that publishes the plan
-  const bool planned = plan_wave(a, bid, g0, pub && wu == 0, up, prefetch_q);
+  const bool planned = plan_wave<kRagged>(a, bid, g0, pub && wu == 0, up, prefetch_q);
   asm volatile("" ::"v"(qpf0), "v"(qpf1));  // the touches have landed (none in flight at any return)
   if (!planned) {
     up.total = plan_units(a, g0, pub, s_tmp, s_unit, reinterpret_cast<int*>(smem));
@@ -869,7 +869,6 @@ void k_partial(PartialArgs a) {
   const bool by_items = planned && ragged;
   const int g = by_items ? up.g : g0, mt = by_items ? up.mt : mt0;
   const int prow = planned ? up.prow : up.first * a.M;
-  __builtin_amdgcn_sched_barrier(0);  // keep the plan's code apart from the unit's
   if (g < 0 || g >= up.total || g >= a.units_cap) return;
   const int key_off = up.key_off;
   const int prefix = up.prefix;
@@ -1577,11 +1576,12 @@ void k_merge(MergeArgs a) {
   const int cl = lane % kLanes, slot = w * kGroups + lane / kLanes;
   const int b = row / a.M, r = row - b * a.M;
   ReqPlan R = a.req[b];
-  const int Mb = R.tree_nodes * a.H;  // the request's rows, and the row stride of its partials
-  if (r >= Mb) return;  // past this request's rows (ragged trees)
+  // the request's rows, and the row stride of its partials (M unless the call is ragged)
+  if (r >= R.tree_nodes * a.H) return;  // past this request's rows (ragged trees)
+  const int Mb = a.ragged ? R.tree_nodes * a.H : a.M;
   const size_t orow = (size_t)R.node_off * a.H + r;  // the row in out / lse
-  const int64_t prow = min(max((int64_t)R.prow, (int64_t)0), (int64_t)a.rows_cap);  // never index past
-  R.units = (int)min((int64_t)R.units, ((int64_t)a.rows_cap - prow) / Mb);          // the partial buffers
+  const int prow = min(max(R.prow, 0), a.rows_cap);  // never index past the partial buffers
+  if ((int64_t)prow + (int64_t)R.units * Mb > a.rows_cap) R.units = (a.rows_cap - prow) / Mb;
   const float* pl = a.part_lse + prow + r;
   const uint16_t* pob = a.part_o + (size_t)(prow + r) * kVdim + c0 + kPer * cl;
   const size_t ustride = (size_t)Mb * kVdim;
@@ -1651,33 +1651,42 @@ static void launch_timed(K kernel, int grid, int block, hipStream_t s, hipEvent_
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(block), 0, s, args);
 }
 
-template <bool kPaged, bool kBigTree, bool kHelp, bool kRG>
+template <bool kPaged, bool kBigTree, bool kHelp, bool kRG, bool kRagged>
 static void launch_partial_t(const PartialArgs& a, int grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-  launch_timed(k_partial<kPaged, kBigTree, kHelp, kRG>, grid, kThreads, s, e0, e1, a);
+  launch_timed(k_partial<kPaged, kBigTree, kHelp, kRG, kRagged>, grid, kThreads, s, e0, e1, a);
 }
 
-template <bool kPaged>
+template <bool kPaged, bool kRagged>
 static void launch_partial_p(const PartialArgs& a, int grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   const bool big = a.T > 64;
   const bool help = a.n_mtiles == 1 && a.M <= 2 * kRowsPerWave && !big;
   const bool rg = a.n_mtiles == 1 && !help;
   if (help)
-    launch_partial_t<kPaged, false, true, false>(a, grid, s, e0, e1);
+    launch_partial_t<kPaged, false, true, false, kRagged>(a, grid, s, e0, e1);
   else if (rg && big)
-    launch_partial_t<kPaged, true, false, true>(a, grid, s, e0, e1);
+    launch_partial_t<kPaged, true, false, true, kRagged>(a, grid, s, e0, e1);
   else if (rg)
-    launch_partial_t<kPaged, false, false, true>(a, grid, s, e0, e1);
+    launch_partial_t<kPaged, false, false, true, kRagged>(a, grid, s, e0, e1);
   else if (big)
-    launch_partial_t<kPaged, true, false, false>(a, grid, s, e0, e1);
+    launch_partial_t<kPaged, true, false, false, kRagged>(a, grid, s, e0, e1);
   else
-    launch_partial_t<kPaged, false, false, false>(a, grid, s, e0, e1);
+    launch_partial_t<kPaged, false, false, false, kRagged>(a, grid, s, e0, e1);
 }
 
+// Calls with a tree size per request run their own instantiations (the plan by M tiles), so
+// that the others carry none of its code.
 hipError_t launch_partial(const PartialArgs& a, int grid, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
-  if (a.page_log2 > 0)
-    launch_partial_p<true>(a, grid, s, start, stop);
-  else
-    launch_partial_p<false>(a, grid, s, start, stop);
+  if (a.page_log2 > 0) {
+    if (a.tree_lens)
+      launch_partial_p<true, true>(a, grid, s, start, stop);
+    else
+      launch_partial_p<true, false>(a, grid, s, start, stop);
+  } else {
+    if (a.tree_lens)
+      launch_partial_p<false, true>(a, grid, s, start, stop);
+    else
+      launch_partial_p<false, false>(a, grid, s, start, stop);
+  }
   return hipGetLastError();
 }
 

@@ -96,6 +96,7 @@ struct MergeArgs {
   float* lse;
   int32_t batch, H, M;   // M = H * (the call's largest T): rows of a request in out / lse
   int32_t rows_cap;      // rows of part_o / part_lse
+  int32_t ragged;        // 1: a tree size per request (its partial rows are packed, H * T_b per unit)
   int32_t units_hint;              // units of one request the plan is expected to make (sizes the merge's rounds)
 };
 
