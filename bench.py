@@ -12,8 +12,9 @@ Before the W warmup steps of each workload, the bench runs untimed calls for 0.3
 the GPU clocks have ramped up (`settle`).  The default run times the 185k-token workload (the
 headline line) and then, with the same
 protocol, every other seeded workload (`per_config`), the measured stream bandwidth of the
-1 GiB flush kernel (`hbm_stream_gbs`, so that %HBM is also given against it) and the
-scattered-read probe on the headline's rows (`gather_probe_gbs`).
+1 GiB flush kernel (`hbm_stream_gbs`, so that %HBM is also given against it), the
+scattered-read probe on the headline's rows (`gather_probe_gbs`) and the ragged batch against
+the same batch padded (`ragged`, as with --op ragged).
 
 With --op relocate it measures Tier-1 relocation instead: one call moves a 185,000-row
 prefix, scattered over the lower half of a 524,288-slot pool, into one run in the upper
@@ -410,17 +411,16 @@ def ragged_counts(cfg: dict, rag: dict) -> dict:
     return dict(keys=keys, kv_bytes=keys * KV_ROW_BYTES, total_bytes=total, flops=2 * h * visible * (576 + 512))
 
 
-def bench_ragged(args) -> int:
+def time_ragged(steps: int, warmup: int, warm: bool, flush) -> dict:
     """Times the ragged call (mlaverify_run_ragged) and the padded call (mlaverify_run on the
     same batch with every request at the largest tree) with the verify protocol: clock settle,
     warmup, caches flushed before each call, one event pair per call, then the library's
-    per-kernel events."""
+    per-kernel events.  Returns both summaries, the speedup and the workload."""
     import torch
 
     import mla_tree_verify_mlaverify_amd as mv
 
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
+    dev = flush.device
     cfg, rag = ragged_workload()
     B, T, H = cfg["batch"], cfg["tree_nodes"], cfg["heads"]
 
@@ -434,7 +434,6 @@ def bench_ragged(args) -> int:
     plens = i32(cfg["prefix_lens"])
     v = mv.Verifier(num_heads=H, max_batch=B, max_tree_nodes=T, max_prefix_len=int(cfg["prefix_lens"].max()),
                     pool_slots=cfg["slots"], sm_scale=cfg["sm_scale"], device=dev)
-    flush = torch.zeros(1 << 28, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
     pq, pidx, ppar = bf16(cfg["q"]), i32(cfg["kv_indices"]), i32(cfg["tree_parent"])
     pout = torch.empty((B * T, H, 512), dtype=torch.bfloat16, device=dev)
@@ -452,25 +451,25 @@ def bench_ragged(args) -> int:
 
     res = {}
     for name, step in (("ragged", ragged), ("padded", padded)):
-        settle(step, flush, args.warm)
-        for _ in range(args.warmup):
-            if not args.warm:
+        settle(step, flush, warm)
+        for _ in range(warmup):
+            if not warm:
                 flush.add_(1.0)
             step()
-        starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-        ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
         torch.cuda.synchronize()
-        for k in range(args.steps):
-            if not args.warm:
+        for k in range(steps):
+            if not warm:
                 flush.add_(1.0)
             starts[k].record(stream)
             step()
             ends[k].record(stream)
         torch.cuda.synchronize()
         call_ms = [a.elapsed_time(b) for a, b in zip(starts, ends)]
-        v.profile_begin(args.steps)
-        for _ in range(args.steps):
-            if not args.warm:
+        v.profile_begin(steps)
+        for _ in range(steps):
+            if not warm:
                 flush.add_(1.0)
             step()
         torch.cuda.synchronize()
@@ -511,19 +510,34 @@ def bench_ragged(args) -> int:
                 "gflop": round(counts["flops"] / 1e9, 2), "roofline": roof}
 
     rs, ps = summary(res["ragged"], rc), summary(res["padded"], pc)
+    del v
+    torch.cuda.empty_cache()
+    return {"config": {"workload": f"ragged_b{B}_ploguniform_t4to{T}_h{H}", "batch": B, "heads": H,
+                       "tree_lens": [int(x) for x in rag["tree_lens"]],
+                       "prefix_lens": [int(x) for x in cfg["prefix_lens"]],
+                       "cache": "warm" if warm else "flushed 1 GiB before each call"},
+            "ragged": rs, "padded": ps,
+            "speedup_vs_padded": round(res["padded"]["med"] / res["ragged"]["med"], 3),
+            "rows": {"ragged": rows * H, "padded": B * T * H},
+            "max_abs_diff_vs_padded_rows": worst, "steps": steps,
+            "ms_per_step": round(res["ragged"]["med"], 5)}
+
+
+def bench_ragged(args) -> int:
+    import torch
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    flush = torch.zeros(1 << 28, dtype=torch.float32, device=dev)
+    r = time_ragged(args.steps, args.warmup, args.warm, flush)
     line = {
-        "metric": RAGGED_METRIC, "value": rs["us_per_call"]["median"], "unit": "us/call", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(res["ragged"]["med"], 5),
+        "metric": RAGGED_METRIC, "value": r["ragged"]["us_per_call"]["median"], "unit": "us/call", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": r["ms_per_step"],
         "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": f"ragged_b{B}_ploguniform_t4to{T}_h{H}", "batch": B, "heads": H,
-                   "tree_lens": [int(x) for x in rag["tree_lens"]],
-                   "prefix_lens": [int(x) for x in cfg["prefix_lens"]],
-                   "cache": "warm" if args.warm else "flushed 1 GiB before each call"},
-        "ragged": rs, "padded": ps,
-        "speedup_vs_padded": round(res["padded"]["med"] / res["ragged"]["med"], 3),
-        "rows": {"ragged": rows * H, "padded": B * T * H},
-        "max_abs_diff_vs_padded_rows": worst,
-        "roofline": rs["roofline"],
+        "config": r["config"], "ragged": r["ragged"], "padded": r["padded"],
+        "speedup_vs_padded": r["speedup_vs_padded"], "rows": r["rows"],
+        "max_abs_diff_vs_padded_rows": r["max_abs_diff_vs_padded_rows"],
+        "roofline": r["ragged"]["roofline"],
     }
     print(json.dumps(line), flush=True)
     return 0
@@ -701,6 +715,8 @@ def main() -> int:
             del r, c
             torch.cuda.empty_cache()
         line["per_config"] = per
+        # the ragged batch (a tree size per request) against the same batch padded
+        line["ragged"] = time_ragged(steps, min(args.warmup, 3), args.warm, flush)
         # the scattered-read ceiling of the two load paths on the headline's own rows
         line["gather_probe_gbs"] = gather_probe(cfg, flush, grids=(512,))
     if not args.no_cpu:
