@@ -6,7 +6,8 @@
 //                 through the page_size=1 index table into LDS and computes
 //                 S^T = K Q^T and O^T += V^T P^T on bf16 MFMA (32x32x16), with the softmax
 //                 kept in registers; the last unit of a request also covers the draft-tree
-//                 keys under the ancestor-or-self bitmask it builds in LDS.
+//                 keys under the ancestor-or-self bitmask it builds in LDS.  A call with a
+//                 tree size per request is planned by M tiles (plan_wave).
 //   k_merge       merges the unit partials of every row by their log-sum-exp.
 //   k_tree_masks  the bitmask step alone (one wave per request).
 //
@@ -792,7 +793,8 @@ template <bool kPaged, class Checks>
 // other workgroup reads the same keys, so every gather goes to HBM, and the compute waves
 // stage their pieces in VGPRs (plain non-temporal 16-byte loads, which reach a higher rate
 // from HBM than direct-to-LDS loads) and write them to LDS at the end of the iteration
-// (tiles 0 and 1 too, except for big trees).
+// (tiles 0 and 1 too, except for big trees).  kRagged: the call has a tree size per request,
+// planned by M tiles (plan_wave) with the workgroup's unit and M tile taken from the plan.
 template <bool kPaged, bool kBigTree, bool kHelp, bool kRG, bool kRagged>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_partial(PartialArgs a) {
