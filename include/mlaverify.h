@@ -147,7 +147,8 @@ MLAVERIFY_API int mlaverify_run(mlaverify_t h, int32_t batch, int32_t tree_nodes
  * request; the reading of the layout below is this library's).  Request b has
  * T_b = tree_lens[b] nodes, 1 <= T_b <= max_T <= max_tree_nodes; max_T (host) sizes the
  * launch, the kernels size each request's work by its own T_b, so a small tree costs no
- * padded rows.  Rows are packed request after request: node i of request b is row n_b + i
+ * padded rows, and (up to 64 requests) the prefix split is chosen over the 128-row tiles the
+ * requests' rows fill, so that requests with fewer rows get shorter units.  Rows are packed request after request: node i of request b is row n_b + i
  * with n_b = T_0 + ... + T_{b-1}.  Device arguments (as for mlaverify_run otherwise):
  *   tree_lens   int32 [batch]
  *   q           bf16 [sum T_b, H, 576], row (n_b + i)*H + h
