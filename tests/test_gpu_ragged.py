@@ -98,6 +98,22 @@ def test_ragged_parity(seed, prefix, tree_lens, heads, split):
     check_ragged_plan(v, case, split)
 
 
+def test_ragged_batch_over_64_requests():
+    # more than 64 requests take the workgroup plan, which plans as if every tree were the
+    # largest (partial rows apart at first_unit * M), with a tree size per request
+    rng = np.random.default_rng(88)
+    prefix = [int(x) for x in rng.integers(0, 400, size=70)]
+    tree_lens = [int(x) for x in rng.integers(1, 13, size=70)]
+    tree_lens[5] = 12
+    case = ragged_case(88, prefix, tree_lens, 4, slots=max(4096, 2 * (sum(prefix) + sum(tree_lens))))
+    out, lse, v = run_ragged(case)
+    assert v.read_device_errors() == 0
+    ref_out, ref_lse = oracle(case)
+    compare(out, lse, ref_out, ref_lse)
+    plan = v.read_plan()
+    assert [r["first_unit"] for r in plan["requests"]] == list(np.cumsum([0] + [r["units"] for r in plan["requests"]][:-1]))
+
+
 def test_ragged_with_equal_trees_is_run_bit_for_bit():
     cfg = synth.small_config(85, batch=3, prefix=[1000, 20, 333], tree_nodes=24, heads=8, slots=8192, q_scale=1.0)
     case = dict(q=cfg["q"], pool=cfg["pool"], kv_indices=cfg["kv_indices"], prefix_lens=cfg["prefix_lens"],
