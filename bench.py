@@ -510,9 +510,13 @@ def time_ragged(steps: int, warmup: int, warm: bool, flush) -> dict:
                 "gflop": round(counts["flops"] / 1e9, 2), "roofline": roof}
 
     rs, ps = summary(res["ragged"], rc), summary(res["padded"], pc)
+    name = f"ragged_b{B}_ploguniform_t4to{T}_h{H}"
+    if not warm:  # HBM bytes per launch of the ragged call from its committed counters
+        rs["roofline"]["traffic"] = stored_traffic(name)
+        rs["profile"] = f"profiles/k_partial_{name}.md" if rs["roofline"]["traffic"] else None
     del v
     torch.cuda.empty_cache()
-    return {"config": {"workload": f"ragged_b{B}_ploguniform_t4to{T}_h{H}", "batch": B, "heads": H,
+    return {"config": {"workload": name, "batch": B, "heads": H,
                        "tree_lens": [int(x) for x in rag["tree_lens"]],
                        "prefix_lens": [int(x) for x in cfg["prefix_lens"]],
                        "cache": "warm" if warm else "flushed 1 GiB before each call"},
