@@ -98,6 +98,24 @@ def test_ragged_parity(seed, prefix, tree_lens, heads, split):
     check_ragged_plan(v, case, split)
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_ragged_random_shapes(seed):
+    # random batches: heads, tree sizes (1 to 2 M tiles and past 64 nodes), prefixes and the
+    # split vary, against the oracle and the plan's host model
+    rng = np.random.default_rng(500 + seed)
+    b = int(rng.integers(2, 13))
+    heads = int(rng.choice([2, 4, 8, 16]))
+    tree_lens = [int(x) for x in rng.integers(1, 81, size=b)]
+    prefix = [int(x) for x in rng.integers(0, 3000, size=b)]
+    split = int(rng.choice([0, 0, 96, 512]))
+    case = ragged_case(500 + seed, prefix, tree_lens, heads, slots=max(4096, 2 * (sum(prefix) + sum(tree_lens))))
+    out, lse, v = run_ragged(case, split=split)
+    assert v.read_device_errors() == 0
+    ref_out, ref_lse = oracle(case)
+    compare(out, lse, ref_out, ref_lse)
+    check_ragged_plan(v, case, split)
+
+
 def test_ragged_batch_over_64_requests():
     # more than 64 requests take the workgroup plan, which plans as if every tree were the
     # largest (partial rows apart at first_unit * M), with a tree size per request
