@@ -116,6 +116,25 @@ def test_ragged_random_shapes(seed):
     check_ragged_plan(v, case, split)
 
 
+def test_ragged_bench_workload_full_size():
+    # the ragged batch bench.py times (8 requests, 1k-131k prefixes, trees of 4-32 nodes, 16
+    # heads), every row against the oracle, in the launch configuration of the bench
+    import bench
+
+    cfg, rag = bench.ragged_workload()
+    case = dict(q=rag["q"], pool=cfg["pool"], kv_indices=rag["kv_indices"], prefix_lens=rag["prefix_lens"],
+                tree_lens=rag["tree_lens"], tree_parent=rag["tree_parent"], heads=cfg["heads"],
+                slots=cfg["slots"], sm_scale=cfg["sm_scale"])
+    v = mv.Verifier(num_heads=cfg["heads"], max_batch=cfg["batch"], max_tree_nodes=cfg["tree_nodes"],
+                    max_prefix_len=int(cfg["prefix_lens"].max()), pool_slots=cfg["slots"],
+                    sm_scale=cfg["sm_scale"], device=DEV)
+    out, lse, v = run_ragged(case, max_t=cfg["tree_nodes"], v=v)
+    assert v.read_device_errors() == 0
+    check_ragged_plan(v, case, 0)
+    ref_out, ref_lse = oracle(case)
+    print(compare(out, lse, ref_out, ref_lse))
+
+
 def test_ragged_batch_over_64_requests():
     # more than 64 requests take the workgroup plan, which plans as if every tree were the
     # largest (partial rows apart at first_unit * M), with a tree size per request
