@@ -223,3 +223,23 @@ def test_ragged_paged_equals_its_expansion_and_oracle(seed, prefix, tree_lens, h
     assert np.array_equal(a, b) and np.array_equal(la, lb)
     ref_out, ref_lse = oracle(flat)
     print(compare(a, la, ref_out, ref_lse))
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_ragged_random_paged(seed):
+    # random ragged batches on paged prefixes: bit-identical to the per-token expansion (same
+    # plan) and matched against the oracle
+    rng = np.random.default_rng(600 + seed)
+    b = int(rng.integers(2, 9))
+    heads = int(rng.choice([4, 8, 16]))
+    tree_lens = [int(x) for x in rng.integers(1, 70, size=b)]
+    prefix = [int(x) for x in rng.integers(0, 2500, size=b)]
+    page = int(rng.choice([16, 64, 256]))
+    paged, flat = paged_ragged_case(600 + seed, prefix, tree_lens, heads, slots=32768, page=page)
+    a, la, v = run_ragged(paged, page_size=page)
+    assert v.read_device_errors() == 0
+    check_ragged_plan(v, paged, 0)
+    b_, lb, _ = run_ragged(flat)
+    assert np.array_equal(a, b_) and np.array_equal(la, lb)
+    ref_out, ref_lse = oracle(flat)
+    compare(a, la, ref_out, ref_lse)
