@@ -52,6 +52,7 @@ Layout layout_for(const mlaverify_config& c) {
     // M tile each (ragged_caps)
     const int u = units_for(c, c.max_batch, T);
     const int n_mt = mtiles_for(c.num_heads, T);
+    if ((int64_t)u * n_mt > INT32_MAX) return Layout{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, -1, (int64_t)INT32_MAX + 1};
     if (u * n_mt > units_cap) units_cap = u * n_mt;
     const int64_t rows = std::max((int64_t)u * c.num_heads * T, (int64_t)u * n_mt * kRowsPerBlock);
     if (rows > rows_cap) rows_cap = rows;
@@ -176,7 +177,7 @@ int enqueue_run(const mlaverify_config& c, const RunAreas& w, int batch, int T, 
   // request fills and keeps the weighted count within n_mt * units_grid (the grid), so it
   // makes at most that many units, each of at most kRowsPerBlock rows per M tile.
   ka.units_cap = tree_lens ? n_mt * units_grid : units_grid;
-  ka.rows_cap = tree_lens ? n_mt * units_grid * kRowsPerBlock : units_grid * M;
+  ka.rows_cap = (int32_t)(tree_lens ? (int64_t)n_mt * units_grid * kRowsPerBlock : (int64_t)units_grid * M);
   ka.scale_log2 = c.sm_scale * 1.4426950408889634f;
   ka.flags = c.flags;
   ka.page_log2 = page_log2(c.page_size);
@@ -260,6 +261,9 @@ int mlaverify_validate_config(const mlaverify_config* c) {
     return MLAVERIFY_ERR_UNSUPPORTED;
   if (c->split_tokens > 0 && (int64_t)c->max_batch * cdiv(c->max_prefix_len > 0 ? c->max_prefix_len : 1, c->split_tokens) > (1 << 24))
     return MLAVERIFY_ERR_UNSUPPORTED;
+  // partial rows and unit-table entries are indexed with 32-bit integers on the device
+  const Layout L = layout_for(*c);
+  if (L.rows_cap > INT32_MAX || L.units_cap < 0) return MLAVERIFY_ERR_UNSUPPORTED;
   return MLAVERIFY_OK;
 }
 

@@ -77,6 +77,8 @@ def base_cfg(**kw):
     (dict(page_size=2048), binding.ERR_INVALID_ARG),  # larger than 1024
     (dict(page_size=-4), binding.ERR_INVALID_ARG),
     (dict(max_batch=1024, max_prefix_len=1 << 22), binding.ERR_UNSUPPORTED),  # 32-bit key offsets
+    (dict(num_heads=128, max_batch=64, max_tree_nodes=256, max_prefix_len=1 << 24, split_tokens=1024),
+     binding.ERR_UNSUPPORTED),  # key offsets fit, partial rows pass 2^31 (32-bit row indices)
 ])
 def test_validate_config(lib, kw, expect):
     assert binding.validate_config(base_cfg(**kw)) == expect
