@@ -96,7 +96,8 @@ typedef struct mlaverify_config {
 
 /* Checks a configuration without touching the GPU.  Returns MLAVERIFY_OK,
  * MLAVERIFY_ERR_INVALID_ARG or MLAVERIFY_ERR_UNSUPPORTED.  The limits it checks follow
- * from the kernels (one rank's heads, up to 256 tree nodes, 32-bit segment offsets); the
+ * from the kernels (one rank's heads, up to 256 tree nodes, 32-bit segment offsets, unit
+ * counts and partial-row indices); the
  * pages fix none of them beyond page_size=1 ("Chunk 66.0" summary), which is the default. */
 MLAVERIFY_API int mlaverify_validate_config(const mlaverify_config* cfg);
 
